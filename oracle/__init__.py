@@ -1,0 +1,200 @@
+"""Python access to the CPU oracle (oracle.c) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It marshals numpy arrays into the plain C reference and
+adds no arithmetic of its own.  bf16 values travel as their uint16 bit
+patterns.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+ROUND_SR = 0
+ROUND_RNE = 1
+
+OK = 0
+EINVAL = -1
+ENOTDIVISIBLE = -2
+ERANGE = -3
+ETABLE = -5
+
+TENSOR_DTYPE = np.dtype([("offset", "<u8"), ("numel", "<u8"), ("flags", "<u4"), ("pad", "<u4")])
+
+
+class _HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("bias_correction", ctypes.c_int32)]
+
+
+_u8 = ctypes.c_uint8
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_vp = ctypes.c_void_p
+
+_LIB = None
+
+
+def _load():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    sig = {
+        "oracle_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "oracle_bf16_to_f32_array": (None, [_vp, ctypes.c_uint64, _vp]),
+        "oracle_round_nearest_even": (ctypes.c_uint16, [ctypes.c_float]),
+        "oracle_round_stochastic": (ctypes.c_uint16, [ctypes.c_float, ctypes.c_uint16]),
+        "oracle_round_stochastic_array": (None, [_vp, _vp, ctypes.c_uint64, _vp]),
+        "oracle_round_nearest_even_array": (None, [_vp, ctypes.c_uint64, _vp]),
+        "oracle_philox4x32_10": (None, [_u32p, _u32p, _u32p]),
+        "oracle_rng16": (ctypes.c_uint16, [ctypes.c_uint64, ctypes.c_uint64]),
+        "oracle_rng16_fill": (None, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _vp]),
+        "oracle_shard_range": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, _u64p, _u64p]),
+        "oracle_table_check": (ctypes.c_int, [_vp, ctypes.c_uint32, _u64p]),
+        "oracle_decay_mask": (ctypes.c_int, [_vp, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64, _vp]),
+        "oracle_grad_norm": (None, [_vp, ctypes.c_uint64, ctypes.c_float, _f64p, _f32p, _f32p]),
+        "oracle_bias_corrections": (None, [ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.c_int, _f32p, _f32p]),
+        "oracle_adamw_step": (ctypes.c_int, [_vp, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64,
+                                             _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_HParams),
+                                             ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int]),
+        "oracle_master_to_bf16_sr": (None, [_vp, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _need(a, dtype, name):
+    if not isinstance(a, np.ndarray) or a.dtype != np.dtype(dtype) or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"{name} must be a C-contiguous numpy array of {np.dtype(dtype)}")
+    return a
+
+
+def table(entries):
+    """Build a tensor table from (offset, numel, flags) triples."""
+    t = np.zeros(len(entries), dtype=TENSOR_DTYPE)
+    for k, (off, numel, flags) in enumerate(entries):
+        t[k] = (off, numel, flags, 0)
+    return t
+
+
+def hparams(lr, beta1, beta2, eps, weight_decay, bias_correction=True):
+    return _HParams(lr, beta1, beta2, eps, weight_decay, 1 if bias_correction else 0)
+
+
+def bf16_to_f32(h):
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _load().oracle_bf16_to_f32_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def round_nearest_even(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_nearest_even_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def round_stochastic(x, r):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    r = np.ascontiguousarray(np.broadcast_to(r, x.shape), dtype=np.uint16)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_stochastic_array(_ptr(x), _ptr(r), x.size, _ptr(out))
+    return out
+
+
+def philox4x32_10(counter, key):
+    c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in counter])
+    k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+    out = (ctypes.c_uint32 * 4)()
+    _load().oracle_philox4x32_10(c, k, out)
+    return [int(v) for v in out]
+
+
+def rng16(first, count, seed):
+    out = np.empty(count, np.uint16)
+    _load().oracle_rng16_fill(first, count, seed, _ptr(out))
+    return out
+
+
+def shard_range(n, world, rank):
+    """Returns (status, begin, end)."""
+    b = ctypes.c_uint64(0)
+    e = ctypes.c_uint64(0)
+    rc = _load().oracle_shard_range(n, world, rank, ctypes.byref(b), ctypes.byref(e))
+    return rc, b.value, e.value
+
+
+def table_check(tbl):
+    n = ctypes.c_uint64(0)
+    rc = _load().oracle_table_check(_ptr(tbl), len(tbl), ctypes.byref(n))
+    return rc, n.value
+
+
+def decay_mask(tbl, begin, count):
+    out = np.empty(count, np.uint8)
+    rc = _load().oracle_decay_mask(_ptr(tbl), len(tbl), begin, count, _ptr(out))
+    if rc != OK:
+        raise ValueError(f"oracle_decay_mask failed: {rc}")
+    return out
+
+
+def grad_norm(g, max_norm=1.0):
+    """Returns (sumsq, norm, scale)."""
+    g = _need(g, np.uint16, "g")
+    s = ctypes.c_double(0.0)
+    nrm = ctypes.c_float(0.0)
+    sc = ctypes.c_float(0.0)
+    _load().oracle_grad_norm(_ptr(g), g.size, max_norm, ctypes.byref(s), ctypes.byref(nrm), ctypes.byref(sc))
+    return s.value, nrm.value, sc.value
+
+
+def bias_corrections(beta1, beta2, t, bias_correction=True):
+    b1 = ctypes.c_float(0.0)
+    b2 = ctypes.c_float(0.0)
+    _load().oracle_bias_corrections(beta1, beta2, t, 1 if bias_correction else 0,
+                                    ctypes.byref(b1), ctypes.byref(b2))
+    return b1.value, b2.value
+
+
+def adamw_step(tbl, begin, P, G, M, m, v, hp, grad_scale, t, seed, rounding=ROUND_SR):
+    """One step in place over global elements [begin, begin + len(P))."""
+    n = P.size
+    _need(P, np.uint16, "P")
+    _need(G, np.uint16, "G")
+    _need(m, np.float32, "m")
+    _need(v, np.float32, "v")
+    if M is not None:
+        _need(M, np.float32, "M")
+        if M.size != n:
+            raise ValueError("size mismatch")
+    if G.size != n or m.size != n or v.size != n:
+        raise ValueError("size mismatch")
+    rc = _load().oracle_adamw_step(_ptr(tbl), len(tbl), begin, n, _ptr(P), _ptr(G), _ptr(M),
+                                   _ptr(m), _ptr(v), ctypes.byref(hp), grad_scale, t, seed, rounding)
+    if rc != OK:
+        raise ValueError(f"oracle_adamw_step failed: {rc}")
+
+
+def master_to_bf16_sr(M, begin, seed):
+    _need(M, np.float32, "M")
+    out = np.empty(M.size, np.uint16)
+    _load().oracle_master_to_bf16_sr(_ptr(M), begin, M.size, seed, _ptr(out))
+    return out

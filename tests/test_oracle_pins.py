@@ -1,0 +1,424 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself or retypes its formulas: each
+test checks a printed value, a closed form, an exact invariant, a library
+routine that the case reduces to, or brute force on a tiny input.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+from bf16_numerics_amd import workloads as W
+
+
+def bf16_value(bits):
+    """Exact value of bf16 patterns via torch's own bf16 -> float64 widening."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def to_bf16_bits_torch(x32):
+    """Library RNE (torch's fp32 -> bf16 cast) as bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- Philox
+
+
+def test_philox_known_answers(golden):
+    for case in golden("philox4x32_10_kat.json")["cases"]:
+        ctr = [int(x, 16) for x in case["counter"]]
+        key = [int(x, 16) for x in case["key"]]
+        assert o.philox4x32_10(ctr, key) == [int(x, 16) for x in case["out"]]
+
+
+def test_rng16_uniform_chi_square():
+    # 2^22 draws into 4096 bins of the 16-bit value: chi-square with 4095 dof.
+    r = o.rng16(123_456_789, 1 << 22, 0xDEADBEEF)
+    counts = np.bincount(r >> 4, minlength=4096).astype(np.float64)
+    exp = r.size / 4096
+    chi2 = ((counts - exp) ** 2 / exp).sum()
+    z = (chi2 - 4095) / math.sqrt(2 * 4095)
+    assert abs(z) < 5, z
+    # every 16-bit value is reachable and the mean is centred
+    assert abs(r.astype(np.float64).mean() - 32767.5) < 5 * 65536 / math.sqrt(12 * r.size)
+
+
+def test_rng16_neighbours_independent():
+    # Joint distribution of the top 4 bits of neighbouring draws (same Philox
+    # word halves, adjacent words, adjacent groups): 256 bins each.
+    r = o.rng16(0, 1 << 21, 42).astype(np.int64)
+    for lag in (1, 2, 8):
+        a, b = r[:-lag] >> 12, r[lag:] >> 12
+        counts = np.bincount(a * 16 + b, minlength=256).astype(np.float64)
+        exp = a.size / 256
+        chi2 = ((counts - exp) ** 2 / exp).sum()
+        assert abs((chi2 - 255) / math.sqrt(510)) < 5, (lag, chi2)
+
+
+def test_rng16_depends_on_full_64bit_index_and_seed():
+    lo = o.rng16(5, 64, 7)
+    hi = o.rng16(5 + (1 << 35), 64, 7)        # same low 32 bits of the group index
+    other_seed = o.rng16(5, 64, 7 + (1 << 40))  # differs only in the seed's high word
+    assert (lo != hi).mean() > 0.9
+    assert (lo != other_seed).mean() > 0.9
+
+
+# ---------------------------------------------------------------- rounding
+
+
+def _sr_sample_points():
+    rs = np.random.default_rng(2024)
+    lows = [0, 1, 2, 0x7FFF, 0x8000, 0x8001, 0xFFFE, 0xFFFF] + list(rs.integers(0, 1 << 16, 40))
+    his = [0x3F80, 0x3F81, 0x0001, 0x007F, 0x0080, 0x4380, 0x7F7E, 0xBF80, 0x8001, 0xC2F7, 0x8000]
+    pts = []
+    for k, lo in enumerate(lows):
+        hi = his[k % len(his)]
+        pts.append(np.uint32((hi << 16) | int(lo)).view(np.float32))
+    return np.array(pts, dtype=np.float32)
+
+
+def test_sr_rounds_up_for_exactly_lo16_of_the_draws():
+    # Stochastic rounding ("04 · 多 GPU 与混合精度" §2.3): the far neighbour is
+    # taken with probability lo16 / 65536.  Over all 65536 draws it must be
+    # taken exactly lo16 times, and the mean result must be x exactly.
+    r = np.arange(1 << 16, dtype=np.uint16)
+    for x in _sr_sample_points():
+        bits = int(np.float32(x).view(np.uint32))
+        lo16 = bits & 0xFFFF
+        out = o.round_stochastic(np.full(r.size, x, np.float32), r)
+        trunc = bits >> 16
+        assert set(np.unique(out).tolist()) <= {trunc, (trunc + 1) & 0xFFFF}
+        assert int((out != trunc).sum()) == lo16
+        uniq, counts = np.unique(bf16_value(out), return_counts=True)
+        mean = sum(Fraction(float(u)) * int(c) for u, c in zip(uniq, counts)) / (1 << 16)
+        assert mean == Fraction(float(x)), hex(bits)
+
+
+def test_sr_is_identity_on_bf16_values_and_keeps_nan_inf():
+    rs = np.random.default_rng(7)
+    hi = rs.integers(0, 1 << 16, 5000).astype(np.uint32)
+    hi = hi[(hi & 0x7F80) != 0x7F80]                      # finite bf16 patterns
+    x = (hi << 16).view(np.float32)
+    r = rs.integers(0, 1 << 16, x.size).astype(np.uint16)
+    assert np.array_equal(o.round_stochastic(x, r), hi.astype(np.uint16))
+    special = np.array([np.inf, -np.inf, np.nan], np.float32)
+    out = o.round_stochastic(special, np.array([0, 65535, 3], np.uint16))
+    assert out[0] == 0x7F80 and out[1] == 0xFF80 and np.isnan(bf16_value(out[2:3])[0])
+
+
+def test_rne_matches_library_cast():
+    # The round-to-nearest-even reading reduces to torch's fp32 -> bf16 cast.
+    rs = np.random.default_rng(11)
+    bits = rs.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    ties = ((rs.integers(0, 1 << 16, 4096).astype(np.uint32) << 16) | 0x8000)  # exact half-way points
+    edge = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0xFF7F8000, 0x00008000,
+                     0x00018000, 0x80008000, 0x3F808000, 0x3F818000, 0x00000001, 0x807FFFFF], np.uint32)
+    bits = np.concatenate([bits, ties, edge])
+    x = bits.view(np.float32)
+    ours = o.round_nearest_even(x)
+    ref = to_bf16_bits_torch(x)
+    nan = np.isnan(x)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.isnan(bf16_value(ours[nan])).all()
+
+
+def test_rne_exercise5(golden):
+    fx = golden("bf16_round_nearest_exercise5.json")
+    for case in fx["cases"]:
+        out = o.round_nearest_even(np.array([case["value"]], np.float32))
+        assert bf16_value(out)[0] == case["expect"], case["x"]
+    ints = np.arange(0, 1025, dtype=np.float32)
+    back = bf16_value(o.round_nearest_even(ints))
+    exact = ints[back == ints]
+    assert exact.max() >= fx["exact_integers_up_to"]
+    assert np.all(back[: fx["exact_integers_up_to"] + 1] == ints[: fx["exact_integers_up_to"] + 1])
+    assert back[257] != 257
+
+
+def test_rne_stalls_below_half_ulp():
+    # "04 · 多 GPU 与混合精度" §2.3: when the true update stays below half a bf16
+    # step, round-to-nearest discards it every time.
+    rs = np.random.default_rng(3)
+    hi = rs.integers(0x3F00, 0x4000, 2000).astype(np.uint32)  # values in [0.5, 2)
+    x = (hi << 16).view(np.float32).astype(np.float64)
+    ulp = np.where(x < 1.0, 2.0 ** -8, 2.0 ** -7)
+    for frac in (0.1, 0.3, 0.49):
+        moved = (x + frac * ulp).astype(np.float32)
+        assert np.array_equal(o.round_nearest_even(moved), hi.astype(np.uint16))
+
+
+# ---------------------------------------------------------------- shards
+
+
+def test_shard_range_rules(golden):
+    assert o.shard_range(10, 0, 0)[0] == o.EINVAL
+    assert o.shard_range(12, 4, 4)[0] == o.ERANGE
+    assert o.shard_range(10, 4, 0)[0] == o.ENOTDIVISIBLE
+    n = 29568
+    for world in (1, 2, 3, 4, 7, 8, 16):
+        if n % world:
+            assert o.shard_range(n, world, 0)[0] == o.ENOTDIVISIBLE
+            continue
+        spans = [o.shard_range(n, world, r) for r in range(world)]
+        assert all(rc == o.OK for rc, _, _ in spans)
+        assert spans[0][1] == 0 and spans[-1][2] == n
+        assert all(spans[k][2] == spans[k + 1][1] for k in range(world - 1))
+        assert len({e - b for _, b, e in spans}) == 1
+    fx = golden("zero1_state_bytes.json")
+    rc, b, e = o.shard_range(fx["n"], fx["world"], 1)
+    assert rc == o.OK
+    assert fx["adam_state_bytes_per_param"] * fx["n"] == fx["adam_state_bytes_unsharded"]
+    assert fx["adam_state_bytes_per_param"] * (e - b) == fx["adam_state_bytes_per_card"]
+
+
+def test_table_rules_and_decay_mask():
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    assert o.table_check(tbl) == (o.OK, w.n)
+    # brute force: each element's flag is its tensor's (2-D -> 1)
+    expect = np.concatenate([np.full(int(np.prod(s)), 1 if len(s) == 2 else 0, np.uint8) for _, s in w.tensors])
+    assert np.array_equal(o.decay_mask(tbl, 0, w.n), expect)
+    assert np.array_equal(o.decay_mask(tbl, 1000, 5000), expect[1000:6000])
+    assert expect.sum() == 28672                     # the 2-D parameter count of the d=32 model
+    bad = o.table([(0, 10, 1), (11, 5, 0)])           # gap
+    assert o.table_check(bad)[0] == o.ETABLE
+    bad = o.table([(0, 10, 1), (5, 5, 0)])            # overlap
+    assert o.table_check(bad)[0] == o.ETABLE
+    bad = o.table([(0, 10, 3)])                       # undefined flag bit
+    assert o.table_check(bad)[0] == o.ETABLE
+
+
+# ---------------------------------------------------------------- norm
+
+
+def test_norm_closed_form_constant_grads():
+    # G = 2^-10 over 2^24 elements: sum of squares 16, norm 4, clip scale 1/4.
+    g = np.full(1 << 24, 0x3A80, np.uint16)  # bf16 2^-10
+    assert bf16_value(g[:1])[0] == 2.0 ** -10
+    sumsq, norm, scale = o.grad_norm(g, 1.0)
+    assert sumsq == 16.0 and norm == 4.0 and scale == 0.25
+
+
+def test_norm_brute_force_exact_and_extremes():
+    rs = np.random.default_rng(5)
+    for n in (1, 7, 64, 1000):
+        g = rs.integers(0, 1 << 16, n).astype(np.uint16)
+        g = g[(g & 0x7F80) != 0x7F80]
+        exact = sum(Fraction(float(x)) ** 2 for x in bf16_value(g))
+        sumsq, norm, scale = o.grad_norm(g, 1.0)
+        assert abs(Fraction(sumsq) - exact) <= exact * Fraction(1, 10 ** 14)
+        want_norm = math.sqrt(float(exact))
+        if want_norm > float(np.finfo(np.float32).max):
+            assert norm == math.inf and scale == 0.0   # the norm itself overflows binary32
+            continue
+        assert abs(norm - want_norm) <= 1e-6 * want_norm
+        assert scale == (np.float32(1.0) / np.float32(norm) if norm > 1.0 else 1.0)
+    # far outside the fp32-square range: 2^100 and 2^-120 must not overflow or vanish
+    big = np.array([0x7180, 0x7180], np.uint16)         # 2^100
+    assert bf16_value(big[:1])[0] == 2.0 ** 100
+    sumsq, norm, scale = o.grad_norm(big, 1.0)
+    assert sumsq == 2.0 ** 201 and norm == np.float32(2.0 ** 100.5) and scale == np.float32(1.0) / norm
+    tiny = np.array([0x0380] * 4, np.uint16)           # 2^-120
+    assert bf16_value(tiny[:1])[0] == 2.0 ** -120
+    sumsq, norm, scale = o.grad_norm(tiny, 1.0)
+    assert sumsq == 4 * 2.0 ** -240 and norm == np.float32(2.0 ** -119) and scale == 1.0
+    assert o.grad_norm(np.zeros(10, np.uint16), 1.0) == (0.0, 0.0, 1.0)
+    # strict comparison: norm equal to max_norm is not clipped
+    assert o.grad_norm(np.array([0x3F80], np.uint16), 1.0)[2] == 1.0
+
+
+# ---------------------------------------------------------------- update
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def _bits_f32(x):
+    return o.bf16_to_f32(np.asarray(x, np.uint16))
+
+
+def test_bias_correction_multiplier_printed_values(golden):
+    # With correction off and a constant grad, the step is lr times
+    # (1 - b1^t) / sqrt(1 - b2^t) (第 13 讲 §1.7, §7.3 exercise 1).
+    fx = golden("bias_correction_multipliers.json")
+    for case in fx["cases"]:
+        b2, ts, printed = case["beta2"], case["t"], case["printed"]
+        hp = o.hparams(1.0, fx["beta1"], b2, 1e-8, 0.0, bias_correction=False)
+        tbl = o.table([(0, 2, 0)])
+        G = np.array([0x3F80, 0xBA80], np.uint16)      # +1 and -2^-10
+        P = np.zeros(2, np.uint16)
+        m = np.zeros(2, np.float32)
+        v = np.zeros(2, np.float32)
+        got = {}
+        for t in range(1, max(ts) + 1):
+            M = np.zeros(2, np.float32)                # measure each step from 0
+            o.adamw_step(tbl, 0, P, G, M, m, v, hp, 1.0, t, 99, o.ROUND_RNE)
+            got[t] = (-float(M[0]), float(M[1]))
+        for t, p in zip(ts, printed):
+            decimals = len(p.split(".")[1])
+            assert f"{got[t][0]:.{decimals}f}" == p, (b2, t, got[t][0])
+            assert f"{got[t][1]:.{decimals}f}" == p, (b2, t, got[t][1])
+
+
+def test_bias_correction_on_gives_lr_sized_steps():
+    hp = o.hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, bias_correction=True)
+    tbl = o.table([(0, 1, 0)])
+    G = np.array([0x3F80], np.uint16)
+    P = np.zeros(1, np.uint16)
+    m = np.zeros(1, np.float32)
+    v = np.zeros(1, np.float32)
+    for t in range(1, 51):
+        M = np.zeros(1, np.float32)
+        o.adamw_step(tbl, 0, P, G, M, m, v, hp, 1.0, t, 1, o.ROUND_RNE)
+        assert abs(-float(M[0]) / 1e-3 - 1.0) < 1e-5, t
+
+
+def test_decay_only_on_2d_tensors():
+    # "04 · 多 GPU 与混合精度" §2.2: decay applies to 2-D tensors only; with zero
+    # grads the 2-D entries follow p <- old - lr*wd*old and 1-D ones stay put
+    # (第 13 讲 §1.7: theta <- (1 - lr*lambda) theta).
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    rs = np.random.default_rng(9)
+    M = (rs.standard_normal(w.n) * 0.02).astype(np.float32)
+    M0 = M.copy()
+    P = o.round_nearest_even(M)
+    G = np.zeros(w.n, np.uint16)
+    m = np.zeros(w.n, np.float32)
+    v = np.zeros(w.n, np.float32)
+    hp = o.hparams(1e-2, 0.9, 0.95, 1e-8, 0.1)
+    k = 25
+    for t in range(1, k + 1):
+        o.adamw_step(tbl, 0, P, G, M, m, v, hp, 1.0, t, 5, o.ROUND_SR)
+    flags = o.decay_mask(tbl, 0, w.n).astype(bool)
+    assert np.array_equal(M[~flags], M0[~flags])
+    want = M0[flags].astype(np.float64) * (1 - 1e-2 * 0.1) ** k
+    assert np.allclose(M[flags], want, rtol=k * 2e-7, atol=0)
+    assert np.all(M[flags] != M0[flags])
+    assert not m.any() and not v.any()
+
+
+def test_matches_torch_adamw_special_case():
+    # With scale a power of two, the fp32 master trajectory is textbook AdamW:
+    # compare against torch.optim.AdamW (two parameter groups: decay / none)
+    # to a few fp32 ulps per step (第 13 讲 §1.6, §1.7).  Op order differs, so
+    # this is not bit-exact.
+    rs = np.random.default_rng(17)
+    n2d, n1d = 3000, 1000
+    n = n2d + n1d
+    tbl = o.table([(0, n2d, 1), (n2d, n1d, 0)])
+    p0 = to_bf16_bits_torch((rs.standard_normal(n) * 0.02).astype(np.float32))
+    M = _bits_f32(p0)
+    P = p0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    scale = 0.5
+    hp = o.hparams(**HP)
+    w2 = torch.nn.Parameter(torch.from_numpy(M[:n2d].copy()))
+    w1 = torch.nn.Parameter(torch.from_numpy(M[n2d:].copy()))
+    opt = torch.optim.AdamW([{"params": [w2], "weight_decay": 0.1}, {"params": [w1], "weight_decay": 0.0}],
+                            lr=1e-3, betas=(0.9, 0.95), eps=1e-8, foreach=False, fused=False)
+    for t in range(1, 17):
+        std = np.where(np.arange(n) % 3 == 0, 1e-6, 1e-3)       # some grads near eps
+        G = to_bf16_bits_torch((rs.standard_normal(n) * std).astype(np.float32))
+        o.adamw_step(tbl, 0, P, G, M, m, v, hp, scale, t, 1234, o.ROUND_SR)
+        gs = torch.from_numpy(_bits_f32(G)) * scale               # exact (power of two)
+        w2.grad, w1.grad = gs[:n2d].clone(), gs[n2d:].clone()
+        opt.step()
+    ref = torch.cat([w2.detach(), w1.detach()]).numpy()
+    st = [opt.state[w2], opt.state[w1]]
+    ref_m = torch.cat([s["exp_avg"] for s in st]).numpy()
+    ref_v = torch.cat([s["exp_avg_sq"] for s in st]).numpy()
+    # Bounds scaled to the arithmetic, not to the (possibly cancelled) result:
+    # per step, half an ulp of M plus a few ulps of an lr-sized update; for m
+    # and v, a few ulps of the grad scale.  A dropped or misplaced term (eps,
+    # decay, bias correction, grad scale via eps) moves these by >= 1e-2.
+    gmag = np.where(np.arange(n) % 3 == 0, 1e-6, 1e-3) * scale * 4
+    assert np.all(np.abs(M.astype(np.float64) - ref) <= 16 * (np.spacing(np.abs(ref)) + 1e-3 * 1e-6))
+    assert np.all(np.abs(m.astype(np.float64) - ref_m) <= 1e-6 * gmag)
+    assert np.all(np.abs(v.astype(np.float64) - ref_v) <= 1e-6 * gmag ** 2)
+
+
+def test_replay_rebuilds_bf16_bit_exactly():
+    # "04 · 多 GPU 与混合精度" §5.2: rounding the saved master again with the
+    # last update's draws gives back the same bf16 weights.
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    rs = np.random.default_rng(21)
+    P = to_bf16_bits_torch((rs.standard_normal(w.n) * 0.02).astype(np.float32))
+    M = _bits_f32(P)
+    m = np.zeros(w.n, np.float32)
+    v = np.zeros(w.n, np.float32)
+    hp = o.hparams(**HP)
+    for t in range(1, 4):
+        G = to_bf16_bits_torch((rs.standard_normal(w.n) * 1e-3).astype(np.float32))
+        seed = (1337 << 32) | t
+        o.adamw_step(tbl, 0, P, G, M, m, v, hp, 1.0, t, seed, o.ROUND_SR)
+    assert np.array_equal(o.master_to_bf16_sr(M, 0, (1337 << 32) | 3), P)
+    assert not np.array_equal(o.master_to_bf16_sr(M, 0, (1337 << 32) | 2), P)
+
+
+def test_shard_concatenation_is_bit_identical():
+    # 第 13 讲 §5.2: ZeRO-1 over 4 cards gives max difference 0 against data
+    # parallel.  Running each 1/N slice separately must rebuild the unsharded
+    # result bit for bit, because every draw is keyed on the global index.
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    rs = np.random.default_rng(33)
+    P0 = to_bf16_bits_torch((rs.standard_normal(w.n) * 0.02).astype(np.float32))
+    Gs = [to_bf16_bits_torch((rs.standard_normal(w.n) * 1e-3).astype(np.float32)) for _ in range(3)]
+    hp = o.hparams(**HP)
+
+    def run(world):
+        out = []
+        for r in range(world):
+            rc, b, e = o.shard_range(w.n, world, r)
+            assert rc == o.OK
+            P = P0[b:e].copy()
+            M = _bits_f32(P)
+            m = np.zeros(e - b, np.float32)
+            v = np.zeros(e - b, np.float32)
+            for t, G in enumerate(Gs, 1):
+                o.adamw_step(tbl, b, P, G[b:e].copy(), M, m, v, hp, 1.0, t, (1337 << 32) | t, o.ROUND_SR)
+            out.append((P, M, m, v))
+        return [np.concatenate(parts) for parts in zip(*out)]
+
+    full = run(1)
+    for world in (2, 4, 8):
+        for a, b in zip(full, run(world)):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_stall_sr_tracks_master_rne_freezes():
+    # 第 13 讲 §2.3 / "04 · 多 GPU 与混合精度" §2.3: updates of ~0.1 bf16 step.
+    # Round-to-nearest on bf16 weights never moves; stochastic rounding drifts
+    # like the fp32 master in expectation.  65,536 elements, 1000 steps.
+    n, steps = 1 << 16, 1000
+    w = W.stall16m()
+    hp = o.hparams(w.hparams.lr, 0.9, 0.95, 1e-8, 0.0)
+    tbl = o.table([(0, n, 0)])
+    rs = np.random.default_rng(1)
+    P0 = to_bf16_bits_torch(rs.uniform(0.5, 2.0, n).astype(np.float32))
+    G = np.full(n, 0xBA80, np.uint16)   # -2^-10
+    assert bf16_value(G[:1])[0] == -(2.0 ** -10)
+    A = [P0.copy(), _bits_f32(P0), np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    B = [P0.copy(), None, np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    C = [P0.copy(), None, np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    for t in range(1, steps + 1):
+        seed = (1337 << 32) | t
+        o.adamw_step(tbl, 0, A[0], G, A[1], A[2], A[3], hp, 1.0, t, seed, o.ROUND_SR)
+        o.adamw_step(tbl, 0, B[0], G, None, B[2], B[3], hp, 1.0, t, seed, o.ROUND_SR)
+        o.adamw_step(tbl, 0, C[0], G, None, C[2], C[3], hp, 1.0, t, seed, o.ROUND_RNE)
+    p0 = bf16_value(P0)
+    drift_master = A[1].astype(np.float64) - p0
+    drift_sr = bf16_value(B[0]) - p0
+    assert abs(drift_master.mean() - 0.78) < 0.01                  # about lr * steps
+    diff = bf16_value(B[0]) - A[1].astype(np.float64)
+    assert abs(drift_sr.mean() - drift_master.mean()) <= 3 * diff.std() / math.sqrt(n)
+    assert np.array_equal(C[0], P0)                                # frozen
