@@ -1,0 +1,260 @@
+"""Thin Python binding of libbf16opt.so (include/bf16opt.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step of the optimizer runs in the library's
+kernels.  Importing this module fails loudly when the library has not been
+built -- there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+from .build import LIB as _LIB_PATH
+
+OK = 0
+EINVAL = -1
+ENOTDIVISIBLE = -2
+ERANGE = -3
+EMISALIGNED = -4
+ETABLE = -5
+EHIP = -6
+EDEVICE = -7
+
+ROUND_SR = 0
+ROUND_RNE = 1
+FLAG_DECAY = 1
+
+# Symbols declared in include/bf16opt.h.
+EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_destroy", "bfo_table_info",
+           "grad_global_norm", "adamw_sr_step", "master_to_bf16_sr", "bfo_rng_dump",
+           "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error")
+
+
+class BfoTensor(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("numel", ctypes.c_uint64),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class AdamwHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("bias_correction", ctypes.c_int32)]
+
+
+NORM_RESULT_BYTES = 16  # bfo_norm_result: double sumsq; float norm; float scale
+
+
+class BfoError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib().bfo_status_string(status).decode()
+        if status == EHIP:
+            msg += f" (hipError {_lib().bfo_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [{status}]")
+        self.status = status
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is not None:
+        return _L
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it first (python -m bf16_numerics_amd.build "
+                          "or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    u64, u32, vp, i32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    pu64 = ctypes.POINTER(ctypes.c_uint64)
+    sig = {
+        "shard_range": (i32, [u64, u32, u32, pu64, pu64]),
+        "bfo_table_create": (i32, [ctypes.POINTER(BfoTensor), u32, u32, u32, ctypes.POINTER(vp)]),
+        "bfo_table_destroy": (i32, [vp]),
+        "bfo_table_info": (i32, [vp, pu64, pu64, pu64]),
+        "grad_global_norm": (i32, [vp, vp, ctypes.c_float, vp, vp]),
+        "adamw_sr_step": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, u64, u64, i32, vp]),
+        "master_to_bf16_sr": (i32, [vp, vp, vp, u64, vp]),
+        "bfo_rng_dump": (i32, [u64, u64, u64, vp, vp]),
+        "bfo_decay_mask_dump": (i32, [vp, vp, vp]),
+        "bfo_status_string": (ctypes.c_char_p, [i32]),
+        "bfo_last_hip_error": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _L = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises ImportError if it was not built)."""
+    return _lib()
+
+
+_lib()  # fail at import time when the library is missing
+
+
+def _check(fn, status):
+    if status != OK:
+        raise BfoError(fn, status)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _arg(t, dtype, count, name, dev):
+    """Device pointer of a contiguous tensor holding exactly `count` elements."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != count:
+        raise ValueError(f"{name} has {t.numel()} elements, the shard has {count}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def shard_range(n, world, rank):
+    b, e = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check("shard_range", _lib().shard_range(n, world, rank, ctypes.byref(b), ctypes.byref(e)))
+    return b.value, e.value
+
+
+def shard_range_status(n, world, rank):
+    b, e = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    rc = _lib().shard_range(n, world, rank, ctypes.byref(b), ctypes.byref(e))
+    return rc, b.value, e.value
+
+
+class Table:
+    """A validated tensor table intersected with one ZeRO-1 shard (device-resident lookup).
+
+    entries: (offset, numel, flags) triples in buffer order; flags bit 0 = decay.
+    Created on the current device; every call must use that device.
+    """
+
+    def __init__(self, entries, world=1, rank=0, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else
+                                   torch.device(device).index or 0)
+        arr = (BfoTensor * max(1, len(entries)))()
+        for k, (off, numel, flags) in enumerate(entries):
+            arr[k].offset, arr[k].numel, arr[k].flags, arr[k].reserved = off, numel, flags, 0
+        h = ctypes.c_void_p(None)
+        with torch.cuda.device(self.device):
+            _check("bfo_table_create", _lib().bfo_table_create(arr, len(entries), world, rank, ctypes.byref(h)))
+        self._h = h
+        n, b, e = ctypes.c_uint64(0), ctypes.c_uint64(0), ctypes.c_uint64(0)
+        _check("bfo_table_info", _lib().bfo_table_info(h, ctypes.byref(n), ctypes.byref(b), ctypes.byref(e)))
+        self.n, self.begin, self.end = n.value, b.value, e.value
+        self.world, self.rank = world, rank
+
+    @property
+    def size(self):
+        return self.end - self.begin
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("table destroyed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            torch.cuda.synchronize(self.device)
+            _check("bfo_table_destroy", _lib().bfo_table_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def new_norm_result(device):
+    """A zeroed device buffer for bfo_norm_result (16 bytes, 16-byte aligned)."""
+    return torch.zeros(2, dtype=torch.float64, device=device)
+
+
+def read_norm_result(res):
+    """(sumsq, norm, scale) from a bfo_norm_result buffer (synchronises)."""
+    raw = res.detach().cpu()
+    sumsq = float(raw[0])
+    tail = raw[1:2].view(torch.float32)
+    return sumsq, float(tail[0]), float(tail[1])
+
+
+def scale_ptr(res):
+    """Address of bfo_norm_result.scale inside a norm-result buffer."""
+    return res.data_ptr() + 12
+
+
+def grad_global_norm(table, grads, out, max_norm=1.0):
+    dev = table.device
+    g = _arg(grads, torch.bfloat16, table.size, "grads", dev)
+    if out.dtype != torch.float64 or out.numel() != 2 or out.device != dev:
+        raise ValueError("out must be new_norm_result(device)")
+    with torch.cuda.device(dev):
+        _check("grad_global_norm", _lib().grad_global_norm(table.handle, g, max_norm,
+                                                           ctypes.c_void_p(out.data_ptr()), _stream(dev)))
+    return out
+
+
+def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
+                  rounding=ROUND_SR):
+    """One fused AdamW step over the shard.  scale: a norm-result buffer
+    (its .scale is used), an int device address, or None for 1.0."""
+    dev = table.device
+    S = table.size
+    p = _arg(params, torch.bfloat16, S, "params", dev)
+    g = _arg(grads, torch.bfloat16, S, "grads", dev)
+    M = _arg(master, torch.float32, S, "master", dev)
+    mm = _arg(m, torch.float32, S, "m", dev)
+    vv = _arg(v, torch.float32, S, "v", dev)
+    if isinstance(scale, torch.Tensor):
+        if scale.dtype != torch.float64 or scale.numel() != 2 or scale.device != dev:
+            raise ValueError("scale must be a norm-result buffer on the table's device")
+        sp = ctypes.c_void_p(scale_ptr(scale))
+    elif scale is None:
+        sp = None
+    else:
+        sp = ctypes.c_void_p(int(scale))
+    h = hp if isinstance(hp, AdamwHParams) else AdamwHParams(
+        hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1 if hp.bias_correction else 0)
+    with torch.cuda.device(dev):
+        _check("adamw_sr_step", _lib().adamw_sr_step(table.handle, p, g, M, mm, vv, ctypes.byref(h), sp,
+                                                     t, seed, rounding, _stream(dev)))
+
+
+def master_to_bf16_sr(table, master, params, seed):
+    dev = table.device
+    M = _arg(master, torch.float32, table.size, "master", dev)
+    p = _arg(params, torch.bfloat16, table.size, "params", dev)
+    with torch.cuda.device(dev):
+        _check("master_to_bf16_sr", _lib().master_to_bf16_sr(table.handle, M, p, seed, _stream(dev)))
+
+
+def rng_dump(first, count, seed, device=None):
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index or 0)
+    out = torch.empty(count, dtype=torch.int16, device=dev)
+    with torch.cuda.device(dev):
+        _check("bfo_rng_dump", _lib().bfo_rng_dump(first, count, seed, ctypes.c_void_p(out.data_ptr()),
+                                                   _stream(dev)))
+    return out
+
+
+def decay_mask_dump(table):
+    dev = table.device
+    out = torch.empty(table.size, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check("bfo_decay_mask_dump", _lib().bfo_decay_mask_dump(table.handle, ctypes.c_void_p(out.data_ptr()),
+                                                                 _stream(dev)))
+    return out

@@ -1,0 +1,266 @@
+// bfo_abi.cpp -- host side of the C ABI declared in include/bf16opt.h:
+// argument checks, ZeRO-1 shard arithmetic, the per-table decay lookup
+// (built and uploaded once) and the kernel launches on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "bfo_internal.hpp"
+
+namespace {
+
+thread_local int gLastHipError = 0;
+
+int hipFail(hipError_t e) {
+    gLastHipError = int(e);
+    return BFO_EHIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct bfo_table_s {
+    uint64_t n = 0, begin = 0, end = 0;
+    uint32_t world = 1, rank = 0;
+    int device = 0;
+    uint64_t nseg = 0, ntiles = 0;
+    void *devBlock = nullptr;        // one allocation holding everything below
+    uint32_t *tile = nullptr;        // [ntiles]
+    uint64_t *segStart = nullptr;    // [nseg + 1], last = UINT64_MAX
+    uint8_t *segFlag = nullptr;      // [nseg]
+    double *normPartials = nullptr;  // [kNormBlocksMax]
+
+    uint64_t S() const { return end - begin; }
+    bfo::DecayView view() const { return {tile, segStart, segFlag}; }
+};
+
+extern "C" {
+
+// "04 · 多 GPU 与混合精度" §3.2 / "LLM 分布式训练实战" §3.1.
+int shard_range(uint64_t n, uint32_t world, uint32_t rank, uint64_t *begin, uint64_t *end) {
+    if (!begin || !end || world == 0) return BFO_EINVAL;
+    if (rank >= world) return BFO_ERANGE;
+    if (n % world != 0) return BFO_ENOTDIVISIBLE;
+    const uint64_t per = n / world;
+    *begin = uint64_t(rank) * per;
+    *end = *begin + per;
+    return BFO_OK;
+}
+
+int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
+                     bfo_table *out) {
+    if (!out || (count > 0 && !tensors)) return BFO_EINVAL;
+    *out = nullptr;
+    if (count >= bfo::kTileMixed) return BFO_ETABLE;  // segment ids must fit in 31 bits
+
+    // Table: contiguous from 0, known flag bits only, no overflow.
+    uint64_t n = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        if (tensors[k].offset != n || (tensors[k].flags & ~BFO_FLAG_DECAY) || tensors[k].reserved)
+            return BFO_ETABLE;
+        if (tensors[k].numel > UINT64_MAX - n) return BFO_ETABLE;
+        n += tensors[k].numel;
+    }
+    uint64_t b = 0, e = 0;
+    int rc = shard_range(n, world, rank, &b, &e);
+    if (rc != BFO_OK) return rc;
+    if (b % 8 != 0) return BFO_EMISALIGNED;
+    const uint64_t S = e - b;
+
+    // Segments: maximal runs of equal decay flag inside [b, e), shard-local.
+    std::vector<uint64_t> segStart;
+    std::vector<uint8_t> segFlag;
+    for (uint32_t k = 0; k < count; ++k) {
+        const uint64_t lo = tensors[k].offset > b ? tensors[k].offset : b;
+        const uint64_t tend = tensors[k].offset + tensors[k].numel;
+        const uint64_t hi = tend < e ? tend : e;
+        if (lo >= hi) continue;
+        const uint8_t f = uint8_t(tensors[k].flags & BFO_FLAG_DECAY);
+        if (segFlag.empty() || segFlag.back() != f) {
+            segStart.push_back(lo - b);
+            segFlag.push_back(f);
+        }
+    }
+    const uint64_t nseg = segFlag.size();
+    segStart.push_back(UINT64_MAX);
+
+    // Tile words: uniform flag, or the segment holding the tile's first element.
+    const uint64_t ntiles = (S + bfo::kTileElems - 1) / bfo::kTileElems;
+    std::vector<uint32_t> tileWord(ntiles ? ntiles : 1, 0u);
+    uint64_t k = 0;
+    for (uint64_t t = 0; t < ntiles; ++t) {
+        const uint64_t t0 = t * bfo::kTileElems;
+        const uint64_t t1 = t0 + bfo::kTileElems < S ? t0 + bfo::kTileElems : S;
+        while (segStart[k + 1] <= t0) ++k;
+        tileWord[t] = segStart[k + 1] >= t1 ? uint32_t(segFlag[k]) : (uint32_t(k) | bfo::kTileMixed);
+    }
+
+    bfo_table_s *tb = new (std::nothrow) bfo_table_s;
+    if (!tb) return BFO_EINVAL;
+    tb->n = n;
+    tb->begin = b;
+    tb->end = e;
+    tb->world = world;
+    tb->rank = rank;
+    tb->nseg = nseg;
+    tb->ntiles = ntiles;
+    hipError_t he = hipGetDevice(&tb->device);
+    if (he != hipSuccess) {
+        delete tb;
+        return hipFail(he);
+    }
+    auto up8 = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+    const uint64_t offTile = 0;
+    const uint64_t offSeg = offTile + up8(tileWord.size() * sizeof(uint32_t));
+    const uint64_t offFlag = offSeg + up8(segStart.size() * sizeof(uint64_t));
+    const uint64_t offNorm = offFlag + up8(segFlag.size() + 1);
+    const uint64_t bytes = offNorm + up8(bfo::kNormBlocksMax * sizeof(double));
+    he = hipMalloc(&tb->devBlock, bytes);
+    if (he != hipSuccess) {
+        delete tb;
+        return hipFail(he);
+    }
+    char *base = static_cast<char *>(tb->devBlock);
+    tb->tile = reinterpret_cast<uint32_t *>(base + offTile);
+    tb->segStart = reinterpret_cast<uint64_t *>(base + offSeg);
+    tb->segFlag = reinterpret_cast<uint8_t *>(base + offFlag);
+    tb->normPartials = reinterpret_cast<double *>(base + offNorm);
+    segFlag.push_back(0);  // keeps the copy non-empty for an empty shard
+    if ((he = hipMemcpy(tb->tile, tileWord.data(), tileWord.size() * sizeof(uint32_t),
+                        hipMemcpyHostToDevice)) != hipSuccess ||
+        (he = hipMemcpy(tb->segStart, segStart.data(), segStart.size() * sizeof(uint64_t),
+                        hipMemcpyHostToDevice)) != hipSuccess ||
+        (he = hipMemcpy(tb->segFlag, segFlag.data(), segFlag.size(), hipMemcpyHostToDevice)) !=
+            hipSuccess) {
+        (void)hipFree(tb->devBlock);
+        delete tb;
+        return hipFail(he);
+    }
+    *out = tb;
+    return BFO_OK;
+}
+
+int bfo_table_destroy(bfo_table table) {
+    if (!table) return BFO_OK;
+    hipError_t he = hipFree(table->devBlock);
+    delete table;
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+int bfo_table_info(bfo_table table, uint64_t *n, uint64_t *begin, uint64_t *end) {
+    if (!table) return BFO_EINVAL;
+    if (n) *n = table->n;
+    if (begin) *begin = table->begin;
+    if (end) *end = table->end;
+    return BFO_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int checkDevice(const bfo_table_s *t) {
+    int dev = -1;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return hipFail(he);
+    return dev == t->device ? BFO_OK : BFO_EDEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
+                     void *stream) {
+    if (!table || !out || (table->S() && !grads)) return BFO_EINVAL;
+    if (!aligned16(grads) || !aligned16(out)) return BFO_EMISALIGNED;
+    int rc = checkDevice(table);
+    if (rc != BFO_OK) return rc;
+    hipError_t he = bfo::launchNorm(grads, table->S(), max_norm, table->normPartials, out,
+                                    static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                  float *v, const bfo_adamw_hparams *hp, const float *scale, uint64_t t,
+                  uint64_t seed, int rounding, void *stream) {
+    if (!table || !hp || t == 0) return BFO_EINVAL;
+    if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
+    const uint64_t S = table->S();
+    if (S && (!params || !grads || !m || !v)) return BFO_EINVAL;
+    if (!aligned16(params) || !aligned16(grads) || !aligned16(master) || !aligned16(m) ||
+        !aligned16(v) || (reinterpret_cast<uintptr_t>(scale) & 3u))
+        return BFO_EMISALIGNED;
+    int rc = checkDevice(table);
+    if (rc != BFO_OK) return rc;
+    if (S == 0) return BFO_OK;
+
+    // "第 13 讲" §1.7: bias corrections 1 - beta^t, formed in binary64 and
+    // rounded once to binary32; 1 when correction is off.
+    bfo::StepScalars s;
+    s.lr = hp->lr;
+    s.beta1 = hp->beta1;
+    s.beta2 = hp->beta2;
+    s.eps = hp->eps;
+    s.wd = hp->weight_decay;
+    s.bc1 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta1), double(t))) : 1.0f;
+    s.bc2 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta2), double(t))) : 1.0f;
+
+    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), s, scale,
+                                     table->begin / 8, seed, rounding,
+                                     static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
+                      void *stream) {
+    if (!table) return BFO_EINVAL;
+    const uint64_t S = table->S();
+    if (S && (!master || !params)) return BFO_EINVAL;
+    if (!aligned16(master) || !aligned16(params)) return BFO_EMISALIGNED;
+    int rc = checkDevice(table);
+    if (rc != BFO_OK) return rc;
+    if (S == 0) return BFO_OK;
+    hipError_t he = bfo::launchMasterToBf16(master, params, S, table->begin / 8, seed,
+                                            static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, void *stream) {
+    if (count && !out) return BFO_EINVAL;
+    if (reinterpret_cast<uintptr_t>(out) & 1u) return BFO_EMISALIGNED;
+    if (count > UINT64_MAX - first) return BFO_ERANGE;
+    hipError_t he = bfo::launchRngDump(first, count, seed, out, static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream) {
+    if (!table || (table->S() && !out)) return BFO_EINVAL;
+    int rc = checkDevice(table);
+    if (rc != BFO_OK) return rc;
+    hipError_t he = bfo::launchDecayDump(table->view(), table->S(), out, static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+const char *bfo_status_string(int status) {
+    switch (status) {
+        case BFO_OK: return "ok";
+        case BFO_EINVAL: return "invalid argument";
+        case BFO_ENOTDIVISIBLE: return "buffer length not divisible by the shard count";
+        case BFO_ERANGE: return "rank or range out of bounds";
+        case BFO_EMISALIGNED: return "pointer not 16-byte aligned or shard start not a multiple of 8";
+        case BFO_ETABLE: return "tensor table not contiguous from 0 or undefined flag bits";
+        case BFO_EHIP: return "HIP runtime call failed";
+        case BFO_EDEVICE: return "current device differs from the table's device";
+        default: return "unknown status";
+    }
+}
+
+int bfo_last_hip_error(void) { return gLastHipError; }
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// bfo_internal.hpp -- layout constants and kernel launchers shared by the
+// host ABI (bfo_abi.cpp) and the gfx950 kernels (bfo_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/bf16opt.h"
+
+namespace bfo {
+
+// One workgroup of the streaming kernels: 256 lanes = 4 wave64s.
+constexpr int kBlock = 256;
+// Each lane of the update / rebuild kernels owns kVecPerLane 8-element
+// vectors (16 bytes of bf16, 32 bytes of fp32 per vector and array).
+constexpr int kVecPerLane = 2;
+constexpr uint64_t kTileVecs = uint64_t(kBlock) * kVecPerLane;  // vectors per workgroup
+constexpr uint64_t kTileElems = kTileVecs * 8;                  // elements per workgroup
+// Decay lookup: one 32-bit word per tile.  Bit 31 clear: every element of
+// the tile has the same flag, held in bit 0.  Bit 31 set: the tile crosses a
+// flag change; bits 0..30 give the segment holding the tile's first element.
+constexpr uint32_t kTileMixed = 0x80000000u;
+
+// Grad-norm partition: stage 1 uses normBlocks(S) workgroups, a function of
+// the shard length only, so the summation order never depends on the device.
+constexpr int kNormBlocksMax = 2048;
+constexpr uint64_t kNormVecsPerBlockMin = uint64_t(kBlock) * 8;
+
+inline int normBlocks(uint64_t nvec) {
+    uint64_t nb = (nvec + kNormVecsPerBlockMin - 1) / kNormVecsPerBlockMin;
+    if (nb < 1) nb = 1;
+    if (nb > uint64_t(kNormBlocksMax)) nb = kNormBlocksMax;
+    return int(nb);
+}
+
+// Device view of a table's decay lookup.  Segments are maximal runs of
+// equal flag in shard-local coordinates; segStart has nseg + 1 entries, the
+// last being UINT64_MAX so scans always stop.
+struct DecayView {
+    const uint32_t *tile;
+    const uint64_t *segStart;
+    const uint8_t *segFlag;
+};
+
+struct StepScalars {
+    float lr, beta1, beta2, eps, wd, bc1, bc2;
+};
+
+// Launchers (bfo_kernels.hip).  Shapes are checked by the caller: every
+// pointer addresses S elements (S = shard length), 16-byte aligned.
+hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *partials,
+                      bfo_norm_result *out, hipStream_t stream);
+hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
+                       DecayView dv, StepScalars s, const float *scale, uint64_t group0,
+                       uint64_t seed, int rounding, hipStream_t stream);
+hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, uint64_t group0,
+                              uint64_t seed, hipStream_t stream);
+hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out,
+                         hipStream_t stream);
+hipError_t launchDecayDump(DecayView dv, uint64_t S, uint8_t *out, hipStream_t stream);
+
+}  // namespace bfo

@@ -1,0 +1,485 @@
+// bfo_kernels.hip -- gfx950 kernels of the mixed-precision AdamW step.
+//
+// Every kernel here is bound by HBM bandwidth: each element is touched once
+// per launch, so the design goal is full-width (16-byte) coalesced loads and
+// stores, several in flight per lane, and enough workgroups (>> 256 CUs) to
+// keep every channel busy.  Nothing is a contraction, so there is no MFMA.
+//
+// Floating point.  The update is a fixed sequence of binary32 operations
+// (one IEEE operation per line of the per-element function), built with
+// -ffp-contract=off so the compiler fuses nothing that is not written as
+// fma, and with HIP's default correctly rounded fp32 division and sqrt and
+// fp32 denormal support.  The norm accumulates in binary64, where every
+// square of a bf16 value is exact.
+//
+// Page references (title, section):
+//   "04 · 多 GPU 与混合精度": §2.2 the AdamW element update and the two-FMA
+//     lerp; §2.3 stochastic rounding; §4 grad norm and clip; §5.2 rebuilding
+//     bf16 weights from the master with the same draws.
+//   "第 13 讲：扩大 LLM——优化与并行训练": §1.7 bias correction and
+//     decoupled weight decay.
+//   Philox4x32-10: Salmon, Moraes, Dror, Shaw, SC'11.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bfo_internal.hpp"
+
+namespace bfo {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Counter-based draws: Philox4x32-10.  One block of four 32-bit words serves
+// the aligned group of 8 elements (global index >> 3).
+// ---------------------------------------------------------------------------
+struct U32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U32x4 philox10(uint64_t group, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+    constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+    uint32_t c0 = uint32_t(group), c1 = uint32_t(group >> 32), c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t pa = uint64_t(kMulA) * c0;
+        const uint64_t pb = uint64_t(kMulB) * c2;
+        const uint32_t n0 = uint32_t(pb >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = uint32_t(pa >> 32) ^ c3 ^ k1;
+        c1 = uint32_t(pb);
+        c3 = uint32_t(pa);
+        c0 = n0;
+        c2 = n2;
+        k0 += kWeylA;
+        k1 += kWeylB;
+    }
+    return {c0, c1, c2, c3};
+}
+
+// 16-bit draw of element e (0..7) of a group: word e>>1, low half for even e.
+__device__ __forceinline__ uint32_t drawOf(const U32x4 &w, int e) {
+    const uint32_t word = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+    return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// binary32 -> bf16 write-back.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool isNanBits(uint32_t b) { return (b & 0x7FFFFFFFu) > 0x7F800000u; }
+
+// Stochastic rounding: step the truncated pattern one unit (next bf16 away
+// from zero) when the 16 discarded bits exceed the draw.
+__device__ __forceinline__ uint32_t roundSR(float x, uint32_t r) {
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t h = (b >> 16) + ((b & 0xFFFFu) > r ? 1u : 0u);
+    return isNanBits(b) ? ((b >> 16) | 0x40u) : h;
+}
+
+// Round to nearest even: add just under half a unit, plus the kept LSB.
+__device__ __forceinline__ uint32_t roundRNE(float x) {
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t h = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+    return isNanBits(b) ? ((b >> 16) | 0x40u) : h;
+}
+
+__device__ __forceinline__ float bf16Lo(uint32_t word) { return __uint_as_float(word << 16); }
+__device__ __forceinline__ float bf16Hi(uint32_t word) { return __uint_as_float(word & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// Decay flags of the 8 elements starting at shard-local j0 (bit e = element
+// j0 + e), from the tile word and, inside mixed tiles, the segment list.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t decayMask8(const DecayView &dv, uint32_t tileWord, uint64_t j0) {
+    if (!(tileWord & kTileMixed)) return (tileWord & 1u) ? 0xFFu : 0u;
+    uint32_t k = tileWord & ~kTileMixed;
+    while (dv.segStart[k + 1] <= j0) ++k;
+    uint32_t mask = 0;
+    for (int e = 0; e < 8; ++e) {
+        while (dv.segStart[k + 1] <= j0 + uint64_t(e)) ++k;
+        mask |= uint32_t(dv.segFlag[k] & 1u) << e;
+    }
+    return mask;
+}
+
+// ---------------------------------------------------------------------------
+// One element of the AdamW step.  `w` is the element's decay (wd or 0),
+// `old` the fp32 weight before the step; returns the new fp32 weight.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float adamwElem(float graw, float &m, float &v, float old, float w,
+                                           const StepScalars &s, float scale) {
+    const float g = scale * graw;
+    const float m1 = __builtin_fmaf(s.beta1, m, __builtin_fmaf(-s.beta1, g, g));
+    const float gg = g * g;
+    const float v1 = __builtin_fmaf(s.beta2, v, __builtin_fmaf(-s.beta2, gg, gg));
+    const float mh = m1 / s.bc1;
+    const float vh = v1 / s.bc2;
+    const float den = sqrtf(vh) + s.eps;
+    const float u = mh / den;
+    const float d = w * old;
+    const float sum = u + d;
+    const float q = s.lr * sum;
+    m = m1;
+    v = v1;
+    return old - q;
+}
+
+template <int kRound>
+__device__ __forceinline__ uint32_t writeBack(float p, const U32x4 &draws, int e) {
+    if constexpr (kRound == BFO_ROUND_SR) return roundSR(p, drawOf(draws, e));
+    else return roundRNE(p);
+}
+
+// ---------------------------------------------------------------------------
+// Fused update over full 8-element vectors.  Workgroup `tile` owns vectors
+// [tile * kTileVecs, +kTileVecs); lane t takes vectors t and t + 256 of it,
+// so each load instruction of a wave covers 1 KiB (bf16) or 2 KiB (fp32) of
+// contiguous memory.  All loads of a lane are issued before any math.
+// ---------------------------------------------------------------------------
+template <bool kMaster, int kRound>
+__global__ __launch_bounds__(kBlock) void adamwTileKernel(
+    uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
+    float *__restrict__ Mom, float *__restrict__ Var, uint64_t nvec, DecayView dv, StepScalars s,
+    const float *__restrict__ scalePtr, uint64_t group0, uint32_t key0, uint32_t key1,
+    uint64_t tileBase) {
+    const float scale = scalePtr ? *scalePtr : 1.0f;
+    const uint64_t tile = tileBase + blockIdx.x;
+    const uint32_t tileWord = dv.tile[tile];
+
+    uint4 gv[kVecPerLane], pv[kVecPerLane];
+    float4 ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
+    float4 wa[kVecPerLane], wb[kVecPerLane];
+    uint64_t qv[kVecPerLane];
+    bool ok[kVecPerLane];
+
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        qv[k] = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        ok[k] = qv[k] < nvec;
+        if (ok[k]) {
+            const uint64_t q = qv[k];
+            gv[k] = reinterpret_cast<const uint4 *>(G)[q];
+            ma[k] = reinterpret_cast<const float4 *>(Mom)[2 * q];
+            mb[k] = reinterpret_cast<const float4 *>(Mom)[2 * q + 1];
+            va[k] = reinterpret_cast<const float4 *>(Var)[2 * q];
+            vb[k] = reinterpret_cast<const float4 *>(Var)[2 * q + 1];
+            if constexpr (kMaster) {
+                wa[k] = reinterpret_cast<const float4 *>(M)[2 * q];
+                wb[k] = reinterpret_cast<const float4 *>(M)[2 * q + 1];
+            } else {
+                pv[k] = reinterpret_cast<const uint4 *>(P)[q];
+            }
+        }
+    }
+
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        if (!ok[k]) continue;
+        const uint64_t q = qv[k];
+        U32x4 draws{0u, 0u, 0u, 0u};
+        if constexpr (kRound == BFO_ROUND_SR) draws = philox10(group0 + q, key0, key1);
+        const uint32_t dmask = decayMask8(dv, tileWord, q * 8);
+
+        float gr[8] = {bf16Lo(gv[k].x), bf16Hi(gv[k].x), bf16Lo(gv[k].y), bf16Hi(gv[k].y),
+                       bf16Lo(gv[k].z), bf16Hi(gv[k].z), bf16Lo(gv[k].w), bf16Hi(gv[k].w)};
+        float mm[8] = {ma[k].x, ma[k].y, ma[k].z, ma[k].w, mb[k].x, mb[k].y, mb[k].z, mb[k].w};
+        float vv[8] = {va[k].x, va[k].y, va[k].z, va[k].w, vb[k].x, vb[k].y, vb[k].z, vb[k].w};
+        float old[8];
+        if constexpr (kMaster) {
+            old[0] = wa[k].x; old[1] = wa[k].y; old[2] = wa[k].z; old[3] = wa[k].w;
+            old[4] = wb[k].x; old[5] = wb[k].y; old[6] = wb[k].z; old[7] = wb[k].w;
+        } else {
+            old[0] = bf16Lo(pv[k].x); old[1] = bf16Hi(pv[k].x);
+            old[2] = bf16Lo(pv[k].y); old[3] = bf16Hi(pv[k].y);
+            old[4] = bf16Lo(pv[k].z); old[5] = bf16Hi(pv[k].z);
+            old[6] = bf16Lo(pv[k].w); old[7] = bf16Hi(pv[k].w);
+        }
+        float pn[8];
+        uint32_t hb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float w = ((dmask >> e) & 1u) ? s.wd : 0.0f;
+            pn[e] = adamwElem(gr[e], mm[e], vv[e], old[e], w, s, scale);
+            hb[e] = writeBack<kRound>(pn[e], draws, e);
+        }
+        reinterpret_cast<float4 *>(Mom)[2 * q] = make_float4(mm[0], mm[1], mm[2], mm[3]);
+        reinterpret_cast<float4 *>(Mom)[2 * q + 1] = make_float4(mm[4], mm[5], mm[6], mm[7]);
+        reinterpret_cast<float4 *>(Var)[2 * q] = make_float4(vv[0], vv[1], vv[2], vv[3]);
+        reinterpret_cast<float4 *>(Var)[2 * q + 1] = make_float4(vv[4], vv[5], vv[6], vv[7]);
+        if constexpr (kMaster) {
+            reinterpret_cast<float4 *>(M)[2 * q] = make_float4(pn[0], pn[1], pn[2], pn[3]);
+            reinterpret_cast<float4 *>(M)[2 * q + 1] = make_float4(pn[4], pn[5], pn[6], pn[7]);
+        }
+        uint4 out;
+        out.x = hb[0] | (hb[1] << 16);
+        out.y = hb[2] | (hb[3] << 16);
+        out.z = hb[4] | (hb[5] << 16);
+        out.w = hb[6] | (hb[7] << 16);
+        reinterpret_cast<uint4 *>(P)[q] = out;
+    }
+}
+
+// The last S % 8 elements (at most 7), one lane each, with scalar accesses.
+template <bool kMaster, int kRound>
+__global__ __launch_bounds__(64) void adamwTailKernel(uint16_t *P, const uint16_t *G, float *M,
+                                                      float *Mom, float *Var, uint64_t j0,
+                                                      uint32_t count, DecayView dv, StepScalars s,
+                                                      const float *scalePtr, uint64_t group,
+                                                      uint32_t key0, uint32_t key1) {
+    const int e = int(threadIdx.x);
+    if (e >= int(count)) return;
+    const uint64_t j = j0 + uint64_t(e);
+    const float scale = scalePtr ? *scalePtr : 1.0f;
+    const uint32_t dmask = decayMask8(dv, dv.tile[j0 / kTileElems], j0);
+    U32x4 draws{0u, 0u, 0u, 0u};
+    if constexpr (kRound == BFO_ROUND_SR) draws = philox10(group, key0, key1);
+    float mm = Mom[j], vv = Var[j];
+    const float old = kMaster ? M[j] : __uint_as_float(uint32_t(P[j]) << 16);
+    const float w = ((dmask >> e) & 1u) ? s.wd : 0.0f;
+    const float p = adamwElem(__uint_as_float(uint32_t(G[j]) << 16), mm, vv, old, w, s, scale);
+    Mom[j] = mm;
+    Var[j] = vv;
+    if constexpr (kMaster) M[j] = p;
+    P[j] = uint16_t(writeBack<kRound>(p, draws, e));
+}
+
+// ---------------------------------------------------------------------------
+// Rebuild bf16 weights from the master: P = SR(M, draw).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
+                                                             uint16_t *__restrict__ P, uint64_t nvec,
+                                                             uint64_t group0, uint32_t key0,
+                                                             uint32_t key1, uint64_t tileBase) {
+    float4 a[kVecPerLane], b[kVecPerLane];
+    uint64_t qv[kVecPerLane];
+    bool ok[kVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        qv[k] = (tileBase + blockIdx.x) * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        ok[k] = qv[k] < nvec;
+        if (ok[k]) {
+            a[k] = reinterpret_cast<const float4 *>(M)[2 * qv[k]];
+            b[k] = reinterpret_cast<const float4 *>(M)[2 * qv[k] + 1];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        if (!ok[k]) continue;
+        const U32x4 d = philox10(group0 + qv[k], key0, key1);
+        uint4 out;
+        out.x = roundSR(a[k].x, drawOf(d, 0)) | (roundSR(a[k].y, drawOf(d, 1)) << 16);
+        out.y = roundSR(a[k].z, drawOf(d, 2)) | (roundSR(a[k].w, drawOf(d, 3)) << 16);
+        out.z = roundSR(b[k].x, drawOf(d, 4)) | (roundSR(b[k].y, drawOf(d, 5)) << 16);
+        out.w = roundSR(b[k].z, drawOf(d, 6)) | (roundSR(b[k].w, drawOf(d, 7)) << 16);
+        reinterpret_cast<uint4 *>(P)[qv[k]] = out;
+    }
+}
+
+__global__ __launch_bounds__(64) void masterToBf16TailKernel(const float *M, uint16_t *P,
+                                                             uint64_t j0, uint32_t count,
+                                                             uint64_t group, uint32_t key0,
+                                                             uint32_t key1) {
+    const int e = int(threadIdx.x);
+    if (e >= int(count)) return;
+    const U32x4 d = philox10(group, key0, key1);
+    P[j0 + e] = uint16_t(roundSR(M[j0 + e], drawOf(d, e)));
+}
+
+// ---------------------------------------------------------------------------
+// Grad norm.  Stage 1: workgroup b sums the squares of vectors
+// b*256 + t, + nb*256, ... in binary64 (lane-order fixed), reduces its 256
+// lanes in a fixed tree (wave64 butterfly, then 4 waves through LDS) and
+// writes one partial.  Stage 2: one workgroup sums the partials and the
+// ragged tail in a fixed order and derives norm and scale.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double sumSquares8(double acc, const uint4 &x) {
+    const double d0 = double(bf16Lo(x.x)), d1 = double(bf16Hi(x.x));
+    const double d2 = double(bf16Lo(x.y)), d3 = double(bf16Hi(x.y));
+    const double d4 = double(bf16Lo(x.z)), d5 = double(bf16Hi(x.z));
+    const double d6 = double(bf16Lo(x.w)), d7 = double(bf16Hi(x.w));
+    acc = __builtin_fma(d0, d0, acc);
+    acc = __builtin_fma(d1, d1, acc);
+    acc = __builtin_fma(d2, d2, acc);
+    acc = __builtin_fma(d3, d3, acc);
+    acc = __builtin_fma(d4, d4, acc);
+    acc = __builtin_fma(d5, d5, acc);
+    acc = __builtin_fma(d6, d6, acc);
+    acc = __builtin_fma(d7, d7, acc);
+    return acc;
+}
+
+__device__ __forceinline__ double blockSum256(double x) {
+    __shared__ double waveSums[kBlock / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) waveSums[wave] = x;
+    __syncthreads();
+    double total = 0.0;
+    if (threadIdx.x == 0) {
+        total = waveSums[0];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; ++w) total += waveSums[w];
+    }
+    return total;  // valid in lane 0 of wave 0
+}
+
+__global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G,
+                                                           uint64_t nvec, double *__restrict__ partials) {
+    const uint4 *g = reinterpret_cast<const uint4 *>(G);
+    const uint64_t stride = uint64_t(gridDim.x) * kBlock;
+    uint64_t q = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
+    double acc = 0.0;
+    for (; q + 3 * stride < nvec; q += 4 * stride) {
+        const uint4 x0 = g[q], x1 = g[q + stride], x2 = g[q + 2 * stride], x3 = g[q + 3 * stride];
+        acc = sumSquares8(acc, x0);
+        acc = sumSquares8(acc, x1);
+        acc = sumSquares8(acc, x2);
+        acc = sumSquares8(acc, x3);
+    }
+    for (; q < nvec; q += stride) acc = sumSquares8(acc, g[q]);
+    const double total = blockSum256(acc);
+    if (threadIdx.x == 0) partials[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kBlock) void normStage2Kernel(const double *__restrict__ partials, int nb,
+                                                           const uint16_t *__restrict__ tail,
+                                                           uint32_t ntail, float maxNorm,
+                                                           bfo_norm_result *__restrict__ out) {
+    double acc = 0.0;
+    for (int k = threadIdx.x; k < nb; k += kBlock) acc += partials[k];
+    if (threadIdx.x == 0) {
+        for (uint32_t e = 0; e < ntail; ++e) {
+            const double d = double(__uint_as_float(uint32_t(tail[e]) << 16));
+            acc = __builtin_fma(d, d, acc);
+        }
+    }
+    const double sumsq = blockSum256(acc);
+    if (threadIdx.x == 0) {
+        const float norm = float(sqrt(sumsq));
+        const float scale = norm > maxNorm ? maxNorm / norm : 1.0f;
+        out->sumsq = sumsq;
+        out->norm = norm;
+        out->scale = scale;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Test exports.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void rngDumpKernel(uint64_t first, uint64_t count, uint64_t seed,
+                                                        uint16_t *out, uint64_t blockBase) {
+    const uint64_t k = (blockBase + blockIdx.x) * kBlock + threadIdx.x;
+    if (k >= count) return;
+    const uint64_t i = first + k;
+    const U32x4 d = philox10(i >> 3, uint32_t(seed), uint32_t(seed >> 32));
+    out[k] = uint16_t(drawOf(d, int(i & 7)));
+}
+
+__global__ __launch_bounds__(kBlock) void decayDumpKernel(DecayView dv, uint64_t S, uint8_t *out,
+                                                          uint64_t blockBase) {
+    const uint64_t q = (blockBase + blockIdx.x) * kBlock + threadIdx.x;
+    const uint64_t j0 = q * 8;
+    if (j0 >= S) return;
+    const uint32_t mask = decayMask8(dv, dv.tile[j0 / kTileElems], j0);
+    for (int e = 0; e < 8 && j0 + e < S; ++e) out[j0 + e] = uint8_t((mask >> e) & 1u);
+}
+
+// A launch's lane count must stay below 2^32: split long 1-D grids.
+constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 22;
+
+template <bool kMaster, int kRound>
+hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
+                        DecayView dv, StepScalars s, const float *scale, uint64_t group0,
+                        uint64_t seed, hipStream_t stream) {
+    const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
+    const uint64_t nvec = S / 8;
+    const uint32_t ntail = uint32_t(S % 8);
+    if (nvec) {
+        const uint64_t tiles = (nvec + kTileVecs - 1) / kTileVecs;
+        for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
+            const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
+            hipLaunchKernelGGL((adamwTileKernel<kMaster, kRound>), dim3(uint32_t(nb)), dim3(kBlock), 0,
+                               stream, P, G, M, m, v, nvec, dv, s, scale, group0, k0, k1, base);
+        }
+    }
+    if (ntail) {
+        hipLaunchKernelGGL((adamwTailKernel<kMaster, kRound>), dim3(1), dim3(64), 0, stream, P, G, M, m,
+                           v, nvec * 8, ntail, dv, s, scale, group0 + nvec, k0, k1);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *partials,
+                      bfo_norm_result *out, hipStream_t stream) {
+    const uint64_t nvec = S / 8;
+    const uint32_t ntail = uint32_t(S % 8);
+    int nb = 0;
+    if (nvec) {
+        nb = normBlocks(nvec);
+        hipLaunchKernelGGL(normStage1Kernel, dim3(nb), dim3(kBlock), 0, stream, g, nvec, partials);
+    }
+    hipLaunchKernelGGL(normStage2Kernel, dim3(1), dim3(kBlock), 0, stream, partials, nb, g + nvec * 8,
+                       ntail, maxNorm, out);
+    return hipGetLastError();
+}
+
+hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
+                       DecayView dv, StepScalars s, const float *scale, uint64_t group0,
+                       uint64_t seed, int rounding, hipStream_t stream) {
+    if (M) {
+        return rounding == BFO_ROUND_SR
+                   ? launchAdamwT<true, BFO_ROUND_SR>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream)
+                   : launchAdamwT<true, BFO_ROUND_RNE>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream);
+    }
+    return rounding == BFO_ROUND_SR
+               ? launchAdamwT<false, BFO_ROUND_SR>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream)
+               : launchAdamwT<false, BFO_ROUND_RNE>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream);
+}
+
+hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, uint64_t group0,
+                              uint64_t seed, hipStream_t stream) {
+    const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
+    const uint64_t nvec = S / 8;
+    const uint32_t ntail = uint32_t(S % 8);
+    if (nvec) {
+        const uint64_t tiles = (nvec + kTileVecs - 1) / kTileVecs;
+        for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
+            const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
+            hipLaunchKernelGGL(masterToBf16Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P, nvec,
+                               group0, k0, k1, base);
+        }
+    }
+    if (ntail) {
+        hipLaunchKernelGGL(masterToBf16TailKernel, dim3(1), dim3(64), 0, stream, M, P, nvec * 8, ntail,
+                           group0 + nvec, k0, k1);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out,
+                         hipStream_t stream) {
+    if (count) {
+        const uint64_t blocks = (count + kBlock - 1) / kBlock;
+        for (uint64_t base = 0; base < blocks; base += kMaxBlocksPerLaunch) {
+            const uint64_t nb = blocks - base < kMaxBlocksPerLaunch ? blocks - base : kMaxBlocksPerLaunch;
+            hipLaunchKernelGGL(rngDumpKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, first, count, seed,
+                               out, base);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launchDecayDump(DecayView dv, uint64_t S, uint8_t *out, hipStream_t stream) {
+    const uint64_t nv = (S + 7) / 8;
+    if (nv) {
+        const uint64_t blocks = (nv + kBlock - 1) / kBlock;
+        for (uint64_t base = 0; base < blocks; base += kMaxBlocksPerLaunch) {
+            const uint64_t nb = blocks - base < kMaxBlocksPerLaunch ? blocks - base : kMaxBlocksPerLaunch;
+            hipLaunchKernelGGL(decayDumpKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, dv, S, out, base);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bfo

@@ -1,0 +1,192 @@
+/*
+ * bf16opt.h -- C ABI of the MI355X (gfx950) mixed-precision AdamW step.
+ *
+ * The step has three parts and runs over one ZeRO-1 shard of a flat buffer
+ * that holds many tensors back to back:
+ *   1. grad_global_norm: a deterministic L2 norm of the bf16 gradients and
+ *      the clip scale derived from it;
+ *   2. adamw_sr_step: one fused pass per element -- AdamW with lerp-form
+ *      moments, bias correction, decoupled weight decay on flagged (2-D)
+ *      tensors only, an fp32 master update and a bf16 write-back by
+ *      stochastic rounding keyed on (global element index, seed);
+ *   3. master_to_bf16_sr: the resume-time rebuild of the bf16 weights from
+ *      the fp32 master with the same rounding draws.
+ *
+ * Pages defining each operation (title, section):
+ *   "04 · 多 GPU 与混合精度" (llm.c multi-GPU and mixed precision):
+ *     §2.1 precision roles, §2.2 AdamW kernel, §2.3 stochastic rounding,
+ *     §3.2 ZeRO-1 sharding, §4 grad norm and clip, §5.2 bit-perfect resume.
+ *   "第 13 讲：扩大 LLM——优化与并行训练": §1.7 bias correction and AdamW,
+ *     §2.3 fp32 master weights.
+ *   "LLM 分布式训练实战：CUDA/ROCm 多卡并行优化详解": §3.1 sharded update.
+ *
+ * Conventions shared by every entry point
+ *   - Element layout.  A shard is the global element range [begin, end) of
+ *     the flat buffer (see shard_range).  Every array argument is
+ *     shard-local: element j of the array is global element begin + j, and
+ *     the array holds end - begin elements.  bf16 values are passed as their
+ *     16-bit patterns (uint16_t), fp32 values as float.
+ *   - Memory.  Array arguments are device pointers on the device the table
+ *     was created on, 16-byte aligned.  Scalars and the hyperparameter struct
+ *     are host memory.  The caller owns every buffer; the library keeps no
+ *     pointer after a call returns.
+ *   - Asynchrony.  GPU work is queued on `stream` (a hipStream_t; NULL means
+ *     the null stream) and the call returns without waiting for it.  Argument
+ *     errors are reported synchronously and queue no work.  Nothing here
+ *     synchronises the host or allocates memory per call.
+ *   - Errors.  Every function returns BFO_OK (0) or a negative BFO_E* code;
+ *     bfo_status_string() names it.  BFO_EHIP means a HIP runtime call
+ *     failed; bfo_last_hip_error() gives its hipError_t code for the calling
+ *     thread.  The library never prints and never exits.
+ *   - Concurrency.  A table may be used from several threads, but calls on
+ *     one table whose GPU work overlaps in time (different streams without
+ *     ordering) race on the table's norm workspace.
+ */
+#ifndef BF16OPT_H
+#define BF16OPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BFO_OK = 0,
+    BFO_EINVAL = -1,        /* null pointer, world == 0, t == 0, unknown rounding mode */
+    BFO_ENOTDIVISIBLE = -2, /* n is not a multiple of world */
+    BFO_ERANGE = -3,        /* rank >= world */
+    BFO_EMISALIGNED = -4,   /* pointer not 16-byte aligned, or shard start not a multiple of 8 */
+    BFO_ETABLE = -5,        /* table not contiguous from 0, or undefined flag bits set */
+    BFO_EHIP = -6,          /* a HIP runtime call failed */
+    BFO_EDEVICE = -7        /* called with a different current device than the table's */
+};
+
+enum { BFO_ROUND_SR = 0, BFO_ROUND_RNE = 1 };
+
+/* bfo_tensor.flags bit 0: the tensor takes weight decay.  The pages apply
+ * decay to 2-D tensors (embeddings, weight matrices) and not to 1-D ones
+ * (LayerNorm / RMSNorm weights, biases): "04 · 多 GPU 与混合精度" §2.2. */
+#define BFO_FLAG_DECAY 1u
+
+/* One tensor of the flat buffer: global elements [offset, offset + numel).
+ * A table lists the tensors in buffer order; tensor k must start where
+ * tensor k-1 ends, the first at 0; numel may be 0; `reserved` must be 0. */
+typedef struct {
+    uint64_t offset;
+    uint64_t numel;
+    uint32_t flags;
+    uint32_t reserved;
+} bfo_tensor;
+
+/* AdamW hyperparameters ("04 · 多 GPU 与混合精度" §4: lr, beta1 = 0.9,
+ * beta2 = 0.95, eps, weight decay; "第 13 讲" §1.7: bias correction). */
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;     /* used for BFO_FLAG_DECAY tensors; others use 0 */
+    int32_t bias_correction;/* nonzero: divide m by 1 - beta1^t and v by 1 - beta2^t */
+} bfo_adamw_hparams;
+
+/* Output of grad_global_norm, written to device memory (16 bytes). */
+typedef struct {
+    double sumsq;  /* sum of squares of the shard's widened bf16 grads, binary64 */
+    float norm;    /* (float)sqrt(sumsq) */
+    float scale;   /* max_norm / norm if norm > max_norm, else 1 */
+} bfo_norm_result;
+
+/* Opaque handle: a validated tensor table intersected with one shard, plus
+ * the small device-side lookup it needs (created once, reused every step). */
+typedef struct bfo_table_s *bfo_table;
+
+/* ZeRO-1 shard of an n-element buffer over `world` ranks
+ * ("04 · 多 GPU 与混合精度" §3.2: shard = parameter count / process count,
+ * which must divide exactly; "LLM 分布式训练实战" §3.1: rank r starts at
+ * r * (n / world)).  Writes [*begin, *end) = [r*n/world, (r+1)*n/world).
+ * Errors: BFO_EINVAL (world == 0 or null output), BFO_ERANGE (rank >= world),
+ * BFO_ENOTDIVISIBLE (n % world != 0).  Host only; touches no GPU. */
+int shard_range(uint64_t n, uint32_t world, uint32_t rank, uint64_t *begin, uint64_t *end);
+
+/* Validates `tensors` (count entries, host memory, copied), takes rank
+ * `rank`'s shard of the buffer they describe and uploads the per-shard
+ * decay lookup to the current device.  The shard start must be a multiple
+ * of 8 elements (it always is for world == 1; otherwise n / world must be a
+ * multiple of 8): BFO_EMISALIGNED if not.  Other errors: as shard_range,
+ * BFO_ETABLE, BFO_EINVAL (null out, or null tensors with count > 0),
+ * BFO_EHIP.  The handle holds device memory until bfo_table_destroy. */
+int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
+                     bfo_table *out);
+
+/* Frees the handle and its device memory.  No call queued on the handle may
+ * still be running.  NULL is accepted. */
+int bfo_table_destroy(bfo_table table);
+
+/* Buffer length n and the shard [begin, end) of a table. */
+int bfo_table_info(bfo_table table, uint64_t *n, uint64_t *begin, uint64_t *end);
+
+/* Deterministic global grad norm of one shard ("04 · 多 GPU 与混合精度" §4:
+ * grad_norm, then grad_scale = min(1, 1/grad_norm), i.e. clip to 1.0; under
+ * ZeRO-1 this is the shard's part, which ranks would add before the root).
+ * grads: end - begin bf16 patterns.  out: device bfo_norm_result.  Every
+ * square is formed and summed in binary64 over a fixed partition that
+ * depends only on the shard length, so repeated calls give identical bits.
+ * scale = max_norm / norm when norm > max_norm, else 1.0f (an infinite norm
+ * gives 0, a NaN norm gives 1: non-finite grads are not sanitised, check
+ * norm).  An empty shard gives {0, 0, 1}. */
+int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
+                     void *stream);
+
+/* One AdamW step over the shard ("04 · 多 GPU 与混合精度" §2.2, with the
+ * lerp computed as two fused multiply-adds; "第 13 讲" §1.7 for bias
+ * correction and decoupled decay).  Per element i (global) / j (local):
+ *   g   = scale * f32(grads[j])
+ *   m1  = fma(b1, m[j], fma(-b1, g, g));  v1 = fma(b2, v[j], fma(-b2, g*g, g*g))
+ *   mh  = m1 / bc1;  vh = v1 / bc2;  u = mh / (sqrt(vh) + eps)
+ *   old = master ? master[j] : f32(params[j])
+ *   p   = old - lr * (u + w_i * old),  w_i = weight_decay if i's tensor has
+ *         BFO_FLAG_DECAY else 0
+ *   m[j] = m1; v[j] = v1; master[j] = p (when master != NULL);
+ *   params[j] = SR(p, r16(i, seed)) or RNE(p)
+ * each a single binary32 operation in that order.  bc1/bc2 =
+ * (float)(1 - pow(beta, t)) in binary64, or 1 when bias correction is off.
+ * SR rounds to the next bf16 away from zero when the 16 discarded bits of p
+ * exceed r16, else truncates; r16 is a 16-bit draw of Philox4x32-10 (Salmon
+ * et al., SC'11) with counter (lo32(i>>3), hi32(i>>3), 0, 0) and key
+ * (lo32(seed), hi32(seed)); element i takes output word (i>>1)&3, low half
+ * for even i.  RNE rounds to nearest, ties to even.  NaN stays NaN.
+ * master == NULL selects the no-master path (old weights read from params).
+ * scale: device float (e.g. &out->scale of grad_global_norm), or NULL for 1.
+ * t: 1-based step number (0 -> BFO_EINVAL).  rounding: BFO_ROUND_SR/RNE. */
+int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                  float *v, const bfo_adamw_hparams *hp, const float *scale, uint64_t t,
+                  uint64_t seed, int rounding, void *stream);
+
+/* Resume-time rebuild ("04 · 多 GPU 与混合精度" §5.2): params[j] =
+ * SR(master[j], r16(begin + j, seed)) with the draws of adamw_sr_step, so
+ * passing the seed of the update that produced `master` reproduces its
+ * bf16 output bit for bit. */
+int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
+                      void *stream);
+
+/* Test export: out[k] = r16(first + k, seed) for k < count (device array,
+ * 2-byte aligned).  Any first and count. */
+int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, void *stream);
+
+/* Test export: out[j] = 1 if shard element j's tensor has BFO_FLAG_DECAY,
+ * else 0, as the update kernel sees it (device array of end - begin bytes). */
+int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
+
+/* Static string naming a status code. */
+const char *bfo_status_string(int status);
+
+/* hipError_t code of the last HIP failure seen by the calling thread (0 if none). */
+int bfo_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BF16OPT_H */

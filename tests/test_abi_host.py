@@ -1,0 +1,112 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+symbol include/bf16opt.h declares, and rejects bad arguments before any HIP
+call.  No compute entry point is called with valid device arguments here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "bf16opt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def bfo():
+    from bf16_numerics_amd import binding
+    return binding
+
+
+def test_header_declares_the_four_entry_points():
+    fns = header_functions()
+    for name in ("shard_range", "grad_global_norm", "adamw_sr_step", "master_to_bf16_sr"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(bfo):
+    lib = bfo.library()
+    fns = header_functions()
+    assert fns, "no declarations parsed"
+    for name in fns:
+        assert hasattr(lib, name), name
+    assert sorted(bfo.EXPORTS) == fns
+
+
+def test_status_strings(bfo):
+    lib = bfo.library()
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        s = lib.bfo_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.bfo_status_string(-99).decode() == "unknown status"
+
+
+def test_shard_range_host(bfo):
+    assert bfo.shard_range_status(10, 0, 0)[0] == bfo.EINVAL
+    assert bfo.shard_range_status(12, 4, 4)[0] == bfo.ERANGE
+    assert bfo.shard_range_status(10, 4, 0)[0] == bfo.ENOTDIVISIBLE
+    assert bfo.shard_range(1_557_686_400, 8, 1) == (194_710_800, 389_421_600)
+    assert bfo.shard_range(0, 3, 2) == (0, 0)
+    n = 7 << 37
+    spans = [bfo.shard_range(n, 7, r) for r in range(7)]
+    assert spans[0][0] == 0 and spans[-1][1] == n
+    assert all(spans[k][1] == spans[k + 1][0] for k in range(6))
+
+
+def _create(bfo, entries, world=1, rank=0):
+    arr = (bfo.BfoTensor * max(1, len(entries)))()
+    for k, e in enumerate(entries):
+        arr[k].offset, arr[k].numel, arr[k].flags = e[0], e[1], e[2]
+        arr[k].reserved = e[3] if len(e) > 3 else 0
+    h = ctypes.c_void_p(None)
+    return bfo.library().bfo_table_create(arr, len(entries), world, rank, ctypes.byref(h)), h
+
+
+def test_table_create_rejects_bad_tables_before_touching_the_gpu(bfo):
+    assert _create(bfo, [(0, 10, 1), (11, 5, 0)])[0] == bfo.ETABLE      # gap
+    assert _create(bfo, [(0, 10, 1), (8, 5, 0)])[0] == bfo.ETABLE       # overlap
+    assert _create(bfo, [(1, 10, 1)])[0] == bfo.ETABLE                  # not from 0
+    assert _create(bfo, [(0, 10, 2)])[0] == bfo.ETABLE                  # undefined flag bit
+    assert _create(bfo, [(0, 10, 1, 7)])[0] == bfo.ETABLE               # reserved field set
+    assert _create(bfo, [(0, 2**64 - 1, 0), (2**64 - 1, 5, 0)])[0] == bfo.ETABLE  # overflow
+    assert _create(bfo, [(0, 30, 1)], world=4)[0] == bfo.ENOTDIVISIBLE
+    assert _create(bfo, [(0, 32, 1)], world=4, rank=4)[0] == bfo.ERANGE
+    assert _create(bfo, [(0, 36, 1)], world=4, rank=1)[0] == bfo.EMISALIGNED  # shard start 9
+    assert _create(bfo, [(0, 32, 1)], world=0)[0] == bfo.EINVAL
+    lib = bfo.library()
+    assert lib.bfo_table_create(None, 3, 1, 0, ctypes.byref(ctypes.c_void_p())) == bfo.EINVAL
+    arr = (bfo.BfoTensor * 1)()
+    assert lib.bfo_table_create(arr, 1, 1, 0, None) == bfo.EINVAL
+
+
+def test_entry_points_reject_null_table_and_bad_scalars(bfo):
+    lib = bfo.library()
+    hp = bfo.AdamwHParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    assert lib.grad_global_norm(None, None, 1.0, None, None) == bfo.EINVAL
+    assert lib.adamw_sr_step(None, None, None, None, None, None, ctypes.byref(hp), None, 1, 0, 0, None) == bfo.EINVAL
+    assert lib.master_to_bf16_sr(None, None, None, 0, None) == bfo.EINVAL
+    assert lib.bfo_decay_mask_dump(None, None, None) == bfo.EINVAL
+    assert lib.bfo_table_info(None, None, None, None) == bfo.EINVAL
+    assert lib.bfo_table_destroy(None) == bfo.OK
+    assert lib.bfo_rng_dump(0, 10, 0, None, None) == bfo.EINVAL
+    assert lib.bfo_rng_dump(0, 10, 0, ctypes.c_void_p(1), None) == bfo.EMISALIGNED
+    assert lib.bfo_rng_dump(2**64 - 5, 10, 0, ctypes.c_void_p(16), None) == bfo.ERANGE
+
+
+def test_binding_refuses_a_missing_library(tmp_path, monkeypatch):
+    import importlib
+    import sys
+    from bf16_numerics_amd import build
+    monkeypatch.setattr(build, "LIB", str(tmp_path / "missing.so"))
+    sys.modules.pop("bf16_numerics_amd.binding", None)
+    try:
+        with pytest.raises(ImportError):
+            importlib.import_module("bf16_numerics_amd.binding")
+    finally:
+        monkeypatch.undo()
+        sys.modules.pop("bf16_numerics_amd.binding", None)
+        importlib.import_module("bf16_numerics_amd.binding")

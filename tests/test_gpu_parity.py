@@ -1,0 +1,439 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Every case runs the library's kernels on cuda:0 and the oracle on the host
+from the same seeded inputs.  Draws, shard offsets and decay masks must be
+bit-exact; fp values must meet the bars in gpu_harness.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+from bf16_numerics_amd import workloads as W
+from gpu_harness import (SEED, assert_bf16_parity, assert_f32_parity, assert_norm_parity,
+                         assert_state_parity, dev_bf16, dev_f32, device_state, f32, host_copy,
+                         oracle_hparams, oracle_step, step_seed, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def bfo():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from bf16_numerics_amd import binding
+    torch.cuda.set_device(0)
+    return binding
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def ragged_workload(n_tiles=3, tail=13, seed=4):
+    """Many small tensors (sizes 1..40 and a few large ones), alternating decay
+    flags, n = n_tiles * 4096 + tail: crosses tiles, vectors and the ragged end."""
+    rs = np.random.default_rng(seed)
+    n = n_tiles * 4096 + tail
+    tensors, off = [], 0
+    while off < n:
+        size = int(rs.integers(1, 41)) if rs.random() < 0.8 else int(rs.integers(500, 3000))
+        size = min(size, n - off)
+        shape = (size,) if rs.random() < 0.5 else (1, size)
+        tensors.append((f"t{len(tensors)}", shape))
+        off += size
+    return W.Workload("ragged", tensors, grad_std=0.05, steps=3)
+
+
+def windows(entries, b, e, half=40, n_random=24, seed=0):
+    """Global [lo, hi) ranges around every tensor boundary inside [b, e), the
+    shard ends, and some random places; merged."""
+    pts = {b, e} | {off for off, _, _ in entries if b < off < e}
+    rs = np.random.default_rng(seed)
+    rng = [(max(b, p - half), min(e, p + half)) for p in pts]
+    for x in rs.integers(b, max(b + 1, e - 64), n_random):
+        rng.append((int(x), min(e, int(x) + 64)))
+    rng.sort()
+    merged = []
+    for lo, hi in rng:
+        if hi <= lo:
+            continue
+        if merged and lo <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(merged[-1][1], hi))
+        else:
+            merged.append((lo, hi))
+    return merged
+
+
+# --------------------------------------------------------------------- draws
+
+
+@pytest.mark.parametrize("first,count,seed", [
+    (0, 100_003, 0),
+    (5, 4097, 0xDEADBEEF12345678),
+    ((1 << 35) + 3, 10_001, 7),
+    (6_738_415_616 - 4000, 4000, step_seed(20)),
+    (2 ** 64 - 2000, 1990, 2 ** 64 - 1),
+])
+def test_rng_dump_bit_exact(bfo, first, count, seed):
+    got = bfo.rng_dump(first, count, seed, DEV).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, o.rng16(first, count, seed))
+
+
+# --------------------------------------------------------------------- decay masks
+
+
+def test_decay_mask_tiny_all_shards(bfo):
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    for world in (1, 2, 4, 8):
+        for r in range(world):
+            T = bfo.Table(w.entries(), world, r)
+            got = bfo.decay_mask_dump(T).cpu().numpy()
+            assert np.array_equal(got, o.decay_mask(tbl, T.begin, T.size)), (world, r)
+
+
+def test_decay_mask_ragged_full(bfo):
+    w = ragged_workload(n_tiles=6, tail=5)
+    T = bfo.Table(w.entries())
+    got = bfo.decay_mask_dump(T).cpu().numpy()
+    assert np.array_equal(got, o.decay_mask(o.table(w.entries()), 0, w.n))
+
+
+@pytest.mark.parametrize("make", [W.gpt2_124m, W.gpt2_1p5b_shard, W.llama7b])
+def test_decay_mask_windows_large(bfo, make):
+    w = make()
+    ents = w.entries()
+    tbl = o.table(ents)
+    for r in range(w.world):
+        T = bfo.Table(ents, w.world, r)
+        got = bfo.decay_mask_dump(T)
+        for lo, hi in windows(ents, T.begin, T.end, seed=r):
+            g = got[lo - T.begin:hi - T.begin].cpu().numpy()
+            assert np.array_equal(g, o.decay_mask(tbl, lo, hi - lo)), (w.name, r, lo, hi)
+        del got
+
+
+# --------------------------------------------------------------------- norm
+
+
+def _norm_case(bfo, bits):
+    n = bits.size
+    T = bfo.Table([(0, n, 1)] if n else [])
+    G = dev_bf16(bits, DEV) if n else torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    res = bfo.new_norm_result(DEV)
+    bfo.grad_global_norm(T, G, res, 1.0)
+    got = bfo.read_norm_result(res)
+    ref = o.grad_norm(np.ascontiguousarray(bits, np.uint16), 1.0)
+    assert_norm_parity(got, ref)
+    bfo.grad_global_norm(T, G, res, 1.0)
+    assert bfo.read_norm_result(res) == got          # bitwise repeatable
+    return got
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4096 * 3 + 5, 29_568, 2048 * 8 * 256 + 3, 5_000_011])
+def test_norm_sizes(bfo, n):
+    rs = np.random.default_rng(n)
+    x = (rs.standard_normal(n) * 1e-2).astype(np.float32)
+    bits = W.bf16_bits_numpy(torch, torch.from_numpy(x).to(torch.bfloat16))
+    got = _norm_case(bfo, bits)
+    if n == 0:
+        assert got == (0.0, 0.0, 1.0)
+
+
+def test_norm_closed_form_and_extremes(bfo):
+    assert _norm_case(bfo, np.full(1 << 24, 0x3A80, np.uint16)) == (16.0, 4.0, 0.25)
+    assert _norm_case(bfo, np.zeros(1000, np.uint16)) == (0.0, 0.0, 1.0)
+    big = _norm_case(bfo, np.array([0x7180] * 2 + [0] * 9, np.uint16))     # 2^100: beyond fp32 squares
+    assert big[0] == 2.0 ** 201
+    tiny = _norm_case(bfo, np.array([0x0380] * 4, np.uint16))              # 2^-120
+    assert tiny[0] == 4 * 2.0 ** -240
+    rs = np.random.default_rng(1)
+    bits = rs.integers(0, 1 << 16, 100_000).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]
+    _norm_case(bfo, bits)                                                  # random patterns, norm overflows fp32
+
+
+def test_norm_non_finite(bfo):
+    bits = np.full(1000, 0x3C00, np.uint16)
+    bits[17] = 0x7F80                                                      # +inf
+    got = _norm_case(bfo, bits)
+    assert math.isinf(got[1]) and got[2] == 0.0
+    bits[500] = 0x7FC1                                                     # NaN
+    got = _norm_case(bfo, bits)
+    assert math.isnan(got[1]) and got[2] == 1.0
+
+
+def test_norm_gpt2_124m_and_shards(bfo):
+    w = W.gpt2_124m()
+    G = torch.empty(w.n, dtype=torch.bfloat16, device=DEV)
+    W.fill_grads(torch, w, G, 0, 1)
+    T = bfo.Table(w.entries())
+    res = bfo.new_norm_result(DEV)
+    bfo.grad_global_norm(T, G, res, 1.0)
+    got = bfo.read_norm_result(res)
+    assert_norm_parity(got, o.grad_norm(u16(G), 1.0))
+    assert got[1] > 1.0 and got[2] < 1.0                                   # clipping is active
+    # ZeRO-1: shard sums add up to the global sum of squares
+    parts = 0.0
+    for r in range(4):
+        Tr = bfo.Table(w.entries(), 4, r)
+        bfo.grad_global_norm(Tr, G[Tr.begin:Tr.end], res, 1.0)
+        parts += bfo.read_norm_result(res)[0]
+    assert abs(parts - got[0]) <= 1e-12 * got[0]
+
+
+# --------------------------------------------------------------------- update
+
+
+def run_steps(bfo, w, T, tbl, st, h, steps, rounding=o.ROUND_SR, master=True, free_run=False,
+              begin=0, check_each=True):
+    res = bfo.new_norm_result(DEV)
+    stats = []
+    for t in range(1, steps + 1):
+        W.fill_grads(torch, w, st["G"], begin, t)
+        bfo.grad_global_norm(T, st["G"], res, w.hparams.max_norm)
+        bfo.adamw_sr_step(T, st["P"], st["G"], st["M"] if master else None, st["m"], st["v"], w.hparams, t,
+                          step_seed(t), scale=res, rounding=rounding)
+        h["G"] = u16(st["G"])
+        ref_norm = o.grad_norm(h["G"], w.hparams.max_norm)
+        got_norm = bfo.read_norm_result(res)
+        assert_norm_parity(got_norm, ref_norm)
+        scale = ref_norm[2] if free_run else got_norm[2]
+        oracle_step(tbl, begin, h, w.hparams, scale, t, step_seed(t), rounding)
+        if check_each or t == steps:
+            stats.append(assert_state_parity(host_copy(st), h, f"{w.name} t={t}"))
+    return stats
+
+
+def test_update_tiny_free_run_16_steps(bfo):
+    w = W.tiny()
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV)
+    h = host_copy(st)
+    stats = run_steps(bfo, w, T, o.table(w.entries()), st, h, w.steps, free_run=True)
+    assert all(s == {"P": 0, "M": 0, "m": 0, "v": 0} for s in stats), stats
+    # resume replay: the master alone rebuilds the bf16 weights bit for bit
+    P2 = torch.empty_like(st["P"])
+    bfo.master_to_bf16_sr(T, st["M"], P2, step_seed(w.steps))
+    assert np.array_equal(u16(P2), u16(st["P"]))
+
+
+@pytest.mark.parametrize("master,rounding", [(True, o.ROUND_SR), (True, o.ROUND_RNE),
+                                             (False, o.ROUND_SR), (False, o.ROUND_RNE)])
+@pytest.mark.parametrize("n_tiles,tail", [(3, 13), (1, 0), (0, 5), (5, 7)])
+def test_update_ragged_modes(bfo, master, rounding, n_tiles, tail):
+    w = ragged_workload(n_tiles, tail)
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV, master=master)
+    h = host_copy(st)
+    run_steps(bfo, w, T, o.table(w.entries()), st, h, 3, rounding=rounding, master=master)
+
+
+def test_update_gpt2_124m(bfo):
+    w = W.gpt2_124m()
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV)
+    h = host_copy(st)
+    stats = run_steps(bfo, w, T, o.table(w.entries()), st, h, 3)
+    print("gpt2_124m element mismatches per step:", stats, flush=True)
+
+
+def test_update_is_deterministic(bfo):
+    w = ragged_workload(40, 3)
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV)
+    W.fill_grads(torch, w, st["G"], 0, 1)
+    snap = {k: v.clone() for k, v in st.items()}
+    outs = []
+    for _ in range(2):
+        s2 = {k: v.clone() for k, v in snap.items()}
+        res = bfo.new_norm_result(DEV)
+        bfo.grad_global_norm(T, s2["G"], res)
+        bfo.adamw_sr_step(T, s2["P"], s2["G"], s2["M"], s2["m"], s2["v"], w.hparams, 1, step_seed(1), scale=res)
+        outs.append((bfo.read_norm_result(res), host_copy(s2)))
+    assert outs[0][0] == outs[1][0]
+    for k in ("P", "M", "m", "v"):
+        assert np.array_equal(outs[0][1][k].view(np.uint8), outs[1][1][k].view(np.uint8)), k
+
+
+def test_shard_concatenation_bit_identical(bfo):
+    # Running each 1/N shard separately rebuilds the unsharded result bit for
+    # bit (the draws are keyed on the global index), with the global clip scale.
+    w = W.tiny()
+    base = device_state(w, 0, w.n, DEV)
+    grads = []
+    for t in range(1, 4):
+        W.fill_grads(torch, w, base["G"], 0, t)
+        grads.append(base["G"].clone())
+    Tfull = bfo.Table(w.entries())
+
+    def run(world):
+        st = {k: v.clone() for k, v in base.items()}
+        res = bfo.new_norm_result(DEV)
+        tables = [bfo.Table(w.entries(), world, r) for r in range(world)]
+        for t, G in enumerate(grads, 1):
+            bfo.grad_global_norm(Tfull, G, res)             # the all-reduced norm
+            for T in tables:
+                sl = slice(T.begin, T.end)
+                bfo.adamw_sr_step(T, st["P"][sl], G[sl], st["M"][sl], st["m"][sl], st["v"][sl], w.hparams,
+                                  t, step_seed(t), scale=res)
+        return host_copy(st)
+
+    one = run(1)
+    for world in (2, 4, 8):
+        other = run(world)
+        for k in ("P", "M", "m", "v"):
+            assert np.array_equal(one[k].view(np.uint8), other[k].view(np.uint8)), (world, k)
+
+
+def test_master_to_bf16_sr_special_values(bfo):
+    rs = np.random.default_rng(8)
+    n = 4096 * 2 + 6
+    bits = rs.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    bits[:12] = [0x7F800000, 0xFF800000, 0x7FC00001, 0xFFFFFFFF, 0x7F7FFFFF, 0x00000001,
+                 0x80000001, 0x007FFFFF, 0x00000000, 0x80000000, 0x3F808000, 0xBF80FFFF]
+    M = bits.view(np.float32)
+    T = bfo.Table([(0, n, 0)])
+    P = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    for seed in (0, step_seed(3), 2 ** 64 - 1):
+        bfo.master_to_bf16_sr(T, dev_f32(M, DEV), P, seed)
+        got = u16(P)
+        ref = o.master_to_bf16_sr(M, 0, seed)
+        nan = (ref & 0x7FFF) > 0x7F80
+        assert np.array_equal((got & 0x7FFF) > 0x7F80, nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_update_non_finite_grads(bfo):
+    w = ragged_workload(2, 3)
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV)
+    W.fill_grads(torch, w, st["G"], 0, 1)
+    st["G"][10] = float("nan")
+    st["G"][4000] = float("inf")
+    st["G"][4001] = float("-inf")
+    h = host_copy(st)
+    bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, 1, step_seed(1), scale=None)
+    oracle_step(o.table(w.entries()), 0, h, w.hparams, 1.0, 1, step_seed(1))
+    assert_state_parity(host_copy(st), h, "non-finite")
+
+
+def test_empty_shard(bfo):
+    T = bfo.Table([])
+    res = bfo.new_norm_result(DEV)
+    e16 = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    e32 = torch.empty(0, dtype=torch.float32, device=DEV)
+    bfo.grad_global_norm(T, e16, res)
+    assert bfo.read_norm_result(res) == (0.0, 0.0, 1.0)
+    bfo.adamw_sr_step(T, e16, e16, e32, e32, e32, W.HParams(), 1, 1, scale=res)
+    bfo.master_to_bf16_sr(T, e32, e16, 1)
+    torch.cuda.synchronize()
+
+
+def test_misaligned_and_wrong_size_rejected(bfo):
+    w = W.tiny()
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n + 8, DEV)
+    sl = slice(1, w.n + 1)                               # 2-byte / 4-byte offset views
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.adamw_sr_step(T, st["P"][sl], st["G"][sl], st["M"][sl], st["m"][sl], st["v"][sl], w.hparams, 1, 1)
+    assert e.value.status == bfo.EMISALIGNED
+    with pytest.raises(ValueError):
+        bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, 1, 1)
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.adamw_sr_step(T, st["P"][:w.n], st["G"][:w.n], st["M"][:w.n], st["m"][:w.n], st["v"][:w.n],
+                          w.hparams, 0, 1)
+    assert e.value.status == bfo.EINVAL
+
+
+# --------------------------------------------------------------------- stall
+
+
+def test_stall16m_sr_tracks_master_rne_freezes(bfo):
+    w = W.stall16m()
+    n = w.n
+    T = bfo.Table(w.entries())
+    P0, M0, _, _ = W.init_state(torch, w, 0, n, DEV)
+    G = torch.full((n,), w.grad_const, dtype=torch.bfloat16, device=DEV)
+    runs = {}
+    for name, master, rnd in (("A", True, o.ROUND_SR), ("B", False, o.ROUND_SR), ("C", False, o.ROUND_RNE)):
+        st = {"P": P0.clone(), "M": M0.clone() if master else None,
+              "m": torch.zeros(n, device=DEV), "v": torch.zeros(n, device=DEV), "G": G}
+        h = host_copy(st)
+        for t in range(1, w.steps + 1):
+            bfo.adamw_sr_step(T, st["P"], G, st["M"], st["m"], st["v"], w.hparams, t, step_seed(t),
+                              scale=None, rounding=rnd)
+            if t == 1:   # first step bit-compared in full against the oracle
+                oracle_step(o.table(w.entries()), 0, h, w.hparams, 1.0, 1, step_seed(1), rnd)
+                assert_state_parity(host_copy(st), h, f"stall {name} t=1")
+        runs[name] = st
+    p0 = P0.double()
+    drift_master = runs["A"]["M"].double() - p0
+    drift_sr = runs["B"]["P"].double() - p0
+    diff = runs["B"]["P"].double() - runs["A"]["M"].double()
+    bound = 3 * diff.std().item() / math.sqrt(n)
+    print(f"stall: master drift {drift_master.mean().item():.6f}, SR drift {drift_sr.mean().item():.6f}, "
+          f"3-sigma {bound:.2e}", flush=True)
+    assert abs(drift_master.mean().item() - 0.78) < 0.01
+    assert abs(drift_sr.mean().item() - drift_master.mean().item()) <= bound
+    assert torch.equal(runs["C"]["P"].view(torch.int16), P0.view(torch.int16))
+
+
+# --------------------------------------------------------------------- full sizes
+
+
+def full_size_step(bfo, w, rank, steps=1):
+    """One rank of a full-size workload in the layout the benchmark times:
+    full-length P and G buffers (ZeRO-1), shard-local M, m, v."""
+    ents = w.entries()
+    T = bfo.Table(ents, w.world, rank)
+    b, e = T.begin, T.end
+    S = e - b
+    P_full = torch.empty(w.n if w.world > 1 else 0, dtype=torch.bfloat16, device=DEV)
+    P, M, m, v = W.init_state(torch, w, b, e, DEV)
+    if w.world > 1:
+        P_full.view(torch.int16).fill_(0x7FA5)                             # sentinel NaN pattern
+        P_full[b:e] = P
+        del P
+        P = P_full[b:e]
+    G = torch.empty(S, dtype=torch.bfloat16, device=DEV)
+    st = {"P": P, "M": M, "m": m, "v": v, "G": G}
+    res = bfo.new_norm_result(DEV)
+    tbl = o.table(ents)
+    wins = windows(ents, b, e, seed=rank)
+    for t in range(1, steps + 1):
+        W.fill_grads(torch, w, G, b, t)
+        pre = [host_copy(st, lo - b, hi - b) for lo, hi in wins]
+        bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
+        bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, t, step_seed(t), scale=res)
+        got_norm = bfo.read_norm_result(res)
+        Gh = G.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert_norm_parity(got_norm, o.grad_norm(Gh, w.hparams.max_norm))
+        del Gh
+        for (lo, hi), h in zip(wins, pre):
+            oracle_step(tbl, lo, h, w.hparams, got_norm[2], t, step_seed(t))
+            assert_state_parity(host_copy(st, lo - b, hi - b), h, f"{w.name} r{rank} [{lo},{hi}) t={t}")
+    if w.world > 1:
+        outside = torch.cat([P_full[:b], P_full[e:]]).view(torch.int16)
+        assert bool((outside == 0x7FA5).all()), "a write escaped the shard"
+    return got_norm
+
+
+def test_full_size_gpt2_1p5b_shard(bfo):
+    w = W.gpt2_1p5b_shard()
+    for rank in (1, 0, 7):
+        got = full_size_step(bfo, w, rank, steps=2 if rank == 1 else 1)
+        print(f"gpt2_1p5b rank {rank}: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
+
+
+def test_full_size_llama7b(bfo):
+    w = W.llama7b()
+    got = full_size_step(bfo, w, 0, steps=1)
+    print(f"llama7b: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
+    assert got[2] < 1.0
