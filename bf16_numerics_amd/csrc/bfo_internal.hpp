@@ -21,17 +21,15 @@ constexpr uint64_t kTileElems = kTileVecs * 8;                  // elements per 
 // flag change; bits 0..30 give the segment holding the tile's first element.
 constexpr uint32_t kTileMixed = 0x80000000u;
 
-// Grad-norm partition: stage 1 uses normBlocks(S) workgroups, a function of
-// the shard length only, so the summation order never depends on the device.
-constexpr int kNormBlocksMax = 2048;
-constexpr uint64_t kNormVecsPerBlockMin = uint64_t(kBlock) * 8;
+// Grad-norm partition: stage 1 gives each workgroup one tile of
+// kNormTileVecs vectors (kNormVecPerLane per lane, strided by the block) and
+// writes one binary64 partial per tile; stage 2 sums the partials in a fixed
+// order.  Both depend only on the shard length, never on the device.
+constexpr int kNormVecPerLane = 4;
+constexpr uint64_t kNormTileVecs = uint64_t(kBlock) * kNormVecPerLane;
+constexpr int kNormFinishBlock = 1024;
 
-inline int normBlocks(uint64_t nvec) {
-    uint64_t nb = (nvec + kNormVecsPerBlockMin - 1) / kNormVecsPerBlockMin;
-    if (nb < 1) nb = 1;
-    if (nb > uint64_t(kNormBlocksMax)) nb = kNormBlocksMax;
-    return int(nb);
-}
+inline uint64_t normTiles(uint64_t nvec) { return (nvec + kNormTileVecs - 1) / kNormTileVecs; }
 
 // Device view of a table's decay lookup.  Segments are maximal runs of
 // equal flag in shard-local coordinates; segStart has nseg + 1 entries, the

@@ -284,11 +284,13 @@ __global__ __launch_bounds__(64) void masterToBf16TailKernel(const float *M, uin
 }
 
 // ---------------------------------------------------------------------------
-// Grad norm.  Stage 1: workgroup b sums the squares of vectors
-// b*256 + t, + nb*256, ... in binary64 (lane-order fixed), reduces its 256
-// lanes in a fixed tree (wave64 butterfly, then 4 waves through LDS) and
-// writes one partial.  Stage 2: one workgroup sums the partials and the
-// ragged tail in a fixed order and derives norm and scale.
+// Grad norm.  Stage 1: workgroup b owns vectors [b*1024, (b+1)*1024); lane t
+// loads vectors t, t+256, t+512, t+768 (four 16-byte loads in flight), sums
+// their squares in binary64 in that order, and the 256 lanes are reduced in a
+// fixed tree (wave64 butterfly, then the 4 waves through LDS) into one
+// partial per tile.  Stage 2: one 1024-lane workgroup adds the partials
+// (lane t takes t, t+1024, ... in order), then the ragged tail, in a fixed
+// tree, and derives norm and scale.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double sumSquares8(double acc, const uint4 &x) {
     const double d0 = double(bf16Lo(x.x)), d1 = double(bf16Hi(x.x));
@@ -306,8 +308,10 @@ __device__ __forceinline__ double sumSquares8(double acc, const uint4 &x) {
     return acc;
 }
 
-__device__ __forceinline__ double blockSum256(double x) {
-    __shared__ double waveSums[kBlock / 64];
+// Fixed-order sum over the workgroup; the result is valid in thread 0.
+template <int kThreads>
+__device__ __forceinline__ double blockSum(double x) {
+    __shared__ double waveSums[kThreads / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -317,42 +321,53 @@ __device__ __forceinline__ double blockSum256(double x) {
     if (threadIdx.x == 0) {
         total = waveSums[0];
 #pragma unroll
-        for (int w = 1; w < kBlock / 64; ++w) total += waveSums[w];
+        for (int w = 1; w < kThreads / 64; ++w) total += waveSums[w];
     }
-    return total;  // valid in lane 0 of wave 0
+    return total;
 }
 
 __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G,
-                                                           uint64_t nvec, double *__restrict__ partials) {
+                                                           uint64_t nvec, double *__restrict__ partials,
+                                                           uint64_t tileBase) {
     const uint4 *g = reinterpret_cast<const uint4 *>(G);
-    const uint64_t stride = uint64_t(gridDim.x) * kBlock;
-    uint64_t q = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
-    double acc = 0.0;
-    for (; q + 3 * stride < nvec; q += 4 * stride) {
-        const uint4 x0 = g[q], x1 = g[q + stride], x2 = g[q + 2 * stride], x3 = g[q + 3 * stride];
-        acc = sumSquares8(acc, x0);
-        acc = sumSquares8(acc, x1);
-        acc = sumSquares8(acc, x2);
-        acc = sumSquares8(acc, x3);
+    const uint64_t tile = tileBase + blockIdx.x;
+    const uint64_t base = tile * kNormTileVecs + threadIdx.x;
+    uint4 x[kNormVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kNormVecPerLane; ++k) {
+        const uint64_t q = base + uint64_t(k) * kBlock;
+        x[k] = q < nvec ? g[q] : make_uint4(0u, 0u, 0u, 0u);
     }
-    for (; q < nvec; q += stride) acc = sumSquares8(acc, g[q]);
-    const double total = blockSum256(acc);
-    if (threadIdx.x == 0) partials[blockIdx.x] = total;
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kNormVecPerLane; ++k) acc = sumSquares8(acc, x[k]);
+    const double total = blockSum<kBlock>(acc);
+    if (threadIdx.x == 0) partials[tile] = total;
 }
 
-__global__ __launch_bounds__(kBlock) void normStage2Kernel(const double *__restrict__ partials, int nb,
-                                                           const uint16_t *__restrict__ tail,
-                                                           uint32_t ntail, float maxNorm,
-                                                           bfo_norm_result *__restrict__ out) {
+__global__ __launch_bounds__(kNormFinishBlock) void normStage2Kernel(
+    const double *__restrict__ partials, uint64_t ntiles, const uint16_t *__restrict__ tail,
+    uint32_t ntail, float maxNorm, bfo_norm_result *__restrict__ out) {
+    // Lane t adds partials t, t+1024, t+2048, ... in that order; eight loads
+    // are issued before their adds so the L2 round trips overlap.
     double acc = 0.0;
-    for (int k = threadIdx.x; k < nb; k += kBlock) acc += partials[k];
+    uint64_t k = threadIdx.x;
+    constexpr int kAhead = 8;
+    for (; k + (kAhead - 1) * kNormFinishBlock < ntiles; k += kAhead * kNormFinishBlock) {
+        double p[kAhead];
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) p[j] = partials[k + uint64_t(j) * kNormFinishBlock];
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) acc += p[j];
+    }
+    for (; k < ntiles; k += kNormFinishBlock) acc += partials[k];
     if (threadIdx.x == 0) {
         for (uint32_t e = 0; e < ntail; ++e) {
             const double d = double(__uint_as_float(uint32_t(tail[e]) << 16));
             acc = __builtin_fma(d, d, acc);
         }
     }
-    const double sumsq = blockSum256(acc);
+    const double sumsq = blockSum<kNormFinishBlock>(acc);
     if (threadIdx.x == 0) {
         const float norm = float(sqrt(sumsq));
         const float scale = norm > maxNorm ? maxNorm / norm : 1.0f;
@@ -414,13 +429,14 @@ hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *part
                       bfo_norm_result *out, hipStream_t stream) {
     const uint64_t nvec = S / 8;
     const uint32_t ntail = uint32_t(S % 8);
-    int nb = 0;
-    if (nvec) {
-        nb = normBlocks(nvec);
-        hipLaunchKernelGGL(normStage1Kernel, dim3(nb), dim3(kBlock), 0, stream, g, nvec, partials);
+    const uint64_t ntiles = normTiles(nvec);
+    for (uint64_t base = 0; base < ntiles; base += kMaxBlocksPerLaunch) {
+        const uint64_t nb = ntiles - base < kMaxBlocksPerLaunch ? ntiles - base : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, nvec, partials,
+                           base);
     }
-    hipLaunchKernelGGL(normStage2Kernel, dim3(1), dim3(kBlock), 0, stream, partials, nb, g + nvec * 8,
-                       ntail, maxNorm, out);
+    hipLaunchKernelGGL(normStage2Kernel, dim3(1), dim3(kNormFinishBlock), 0, stream, partials, ntiles,
+                       g + nvec * 8, ntail, maxNorm, out);
     return hipGetLastError();
 }
 
