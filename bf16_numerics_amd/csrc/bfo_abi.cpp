@@ -33,7 +33,7 @@ struct bfo_table_s {
     uint32_t *tile = nullptr;        // [ntiles]
     uint64_t *segStart = nullptr;    // [nseg + 1], last = UINT64_MAX
     uint8_t *segFlag = nullptr;      // [nseg]
-    double *normPartials = nullptr;  // [normTiles(S / 8)], at least 1
+    double *normPartials = nullptr;  // [normTiles(S / 8) + normRuns(...)], at least 1
 
     uint64_t S() const { return end - begin; }
     bfo::DecayView view() const { return {tile, segStart, segFlag}; }
@@ -119,7 +119,8 @@ int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, 
     const uint64_t offSeg = offTile + up8(tileWord.size() * sizeof(uint32_t));
     const uint64_t offFlag = offSeg + up8(segStart.size() * sizeof(uint64_t));
     const uint64_t offNorm = offFlag + up8(segFlag.size() + 1);
-    const uint64_t nNorm = bfo::normTiles(S / 8) > 0 ? bfo::normTiles(S / 8) : 1;
+    const uint64_t nTiles = bfo::normTiles(S / 8);
+    const uint64_t nNorm = nTiles + bfo::normRuns(nTiles) > 0 ? nTiles + bfo::normRuns(nTiles) : 1;
     const uint64_t bytes = offNorm + up8(nNorm * sizeof(double));
     he = hipMalloc(&tb->devBlock, bytes);
     if (he != hipSuccess) {

@@ -23,13 +23,20 @@ constexpr uint32_t kTileMixed = 0x80000000u;
 
 // Grad-norm partition: stage 1 gives each workgroup one tile of
 // kNormTileVecs vectors (kNormVecPerLane per lane, strided by the block) and
-// writes one binary64 partial per tile; stage 2 sums the partials in a fixed
-// order.  Both depend only on the shard length, never on the device.
+// writes one binary64 partial per tile.  When there are more than
+// kNormFinishDirect tiles, an intermediate pass sums each run of
+// kNormReduceRun partials in its own workgroup; stage 2 (one workgroup) sums
+// what is left in a fixed order.  All of it depends only on the shard length.
 constexpr int kNormVecPerLane = 4;
 constexpr uint64_t kNormTileVecs = uint64_t(kBlock) * kNormVecPerLane;
 constexpr int kNormFinishBlock = 1024;
+constexpr uint64_t kNormFinishDirect = 32768;
+constexpr uint64_t kNormReduceRun = 4096;
 
 inline uint64_t normTiles(uint64_t nvec) { return (nvec + kNormTileVecs - 1) / kNormTileVecs; }
+inline uint64_t normRuns(uint64_t ntiles) {
+    return ntiles > kNormFinishDirect ? (ntiles + kNormReduceRun - 1) / kNormReduceRun : 0;
+}
 
 // Device view of a table's decay lookup.  Segments are maximal runs of
 // equal flag in shard-local coordinates; segStart has nseg + 1 entries, the

@@ -288,9 +288,11 @@ __global__ __launch_bounds__(64) void masterToBf16TailKernel(const float *M, uin
 // loads vectors t, t+256, t+512, t+768 (four 16-byte loads in flight), sums
 // their squares in binary64 in that order, and the 256 lanes are reduced in a
 // fixed tree (wave64 butterfly, then the 4 waves through LDS) into one
-// partial per tile.  Stage 2: one 1024-lane workgroup adds the partials
-// (lane t takes t, t+1024, ... in order), then the ragged tail, in a fixed
-// tree, and derives norm and scale.
+// partial per tile.  Large shards (more than kNormFinishDirect tiles) add an
+// intermediate pass: workgroup r sums partials [r*4096, (r+1)*4096) (lane t
+// takes t, t+256, ... in order, then the fixed tree).  Stage 2: one 1024-lane
+// workgroup adds the remaining partials (lane t takes t, t+1024, ... in
+// order), then the ragged tail, in a fixed tree, and derives norm and scale.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double sumSquares8(double acc, const uint4 &x) {
     const double d0 = double(bf16Lo(x.x)), d1 = double(bf16Hi(x.x));
@@ -343,6 +345,24 @@ __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__res
     for (int k = 0; k < kNormVecPerLane; ++k) acc = sumSquares8(acc, x[k]);
     const double total = blockSum<kBlock>(acc);
     if (threadIdx.x == 0) partials[tile] = total;
+}
+
+__global__ __launch_bounds__(kBlock) void normReduceKernel(const double *__restrict__ in, uint64_t count,
+                                                           double *__restrict__ out) {
+    const uint64_t lo = uint64_t(blockIdx.x) * kNormReduceRun;
+    const uint64_t hi = lo + kNormReduceRun < count ? lo + kNormReduceRun : count;
+    constexpr int kPer = int(kNormReduceRun / kBlock);
+    double p[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const uint64_t k = lo + uint64_t(j) * kBlock + threadIdx.x;
+        p[j] = k < hi ? in[k] : 0.0;
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) acc += p[j];
+    const double total = blockSum<kBlock>(acc);
+    if (threadIdx.x == 0) out[blockIdx.x] = total;
 }
 
 __global__ __launch_bounds__(kNormFinishBlock) void normStage2Kernel(
@@ -435,7 +455,17 @@ hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *part
         hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, nvec, partials,
                            base);
     }
-    hipLaunchKernelGGL(normStage2Kernel, dim3(1), dim3(kNormFinishBlock), 0, stream, partials, ntiles,
+    const double *finishIn = partials;
+    uint64_t finishCount = ntiles;
+    const uint64_t runs = normRuns(ntiles);
+    if (runs) {
+        double *second = partials + ntiles;
+        hipLaunchKernelGGL(normReduceKernel, dim3(uint32_t(runs)), dim3(kBlock), 0, stream, partials, ntiles,
+                           second);
+        finishIn = second;
+        finishCount = runs;
+    }
+    hipLaunchKernelGGL(normStage2Kernel, dim3(1), dim3(kNormFinishBlock), 0, stream, finishIn, finishCount,
                        g + nvec * 8, ntail, maxNorm, out);
     return hipGetLastError();
 }

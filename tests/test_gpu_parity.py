@@ -138,10 +138,12 @@ def _norm_case(bfo, bits):
     return got
 
 
-@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4096 * 3 + 5, 29_568, 2048 * 8 * 256 + 3, 5_000_011])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4096 * 3 + 5, 29_568, 2048 * 8 * 256 + 3, 5_000_011,
+                               32_768 * 8192, 32_769 * 8192 + 5])
 def test_norm_sizes(bfo, n):
+    # the last two sizes sit on either side of the intermediate-reduction threshold
     rs = np.random.default_rng(n)
-    x = (rs.standard_normal(n) * 1e-2).astype(np.float32)
+    x = rs.standard_normal(n, dtype=np.float32) * np.float32(1e-2)
     bits = W.bf16_bits_numpy(torch, torch.from_numpy(x).to(torch.bfloat16))
     got = _norm_case(bfo, bits)
     if n == 0:
