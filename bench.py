@@ -80,6 +80,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_1p5b_shard")
     ap.add_argument("--grad-pool", type=int, default=4)
+    ap.add_argument("--layout", choices=("flat", "per_tensor"), default="flat",
+                    help="ZeRO-1 shard layout: contiguous range, or 1/N of every tensor")
+    ap.add_argument("--pad", type=int, default=0,
+                    help="append a 1-D tensor of this many elements (e.g. 8 makes n/8 odd: misaligned shards)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -98,20 +102,37 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     w = W.WORKLOADS[args.workload]()
-    T = bfo.Table(w.entries(), w.world, w.rank)
-    b, e, S = T.begin, T.end, T.size
+    if args.pad:
+        w.tensors = list(w.tensors) + [("pad", (args.pad,))]
+    layout = bfo.LAYOUT_PER_TENSOR if args.layout == "per_tensor" else bfo.LAYOUT_FLAT
+    T = bfo.Table(w.entries(), w.world, w.rank, layout=layout)
+    S = T.size
 
-    # ZeRO-1 layout: full-length bf16 params, shard-local fp32 master/m/v and grads.
-    P_full = torch.empty(w.n if w.world > 1 else 0, dtype=torch.bfloat16, device=dev)
-    P, M, m, v = W.init_state(torch, w, b, e, dev)
-    if w.world > 1:
-        P_full[b:e] = P
-        del P
-        P = P_full[b:e]
+    if layout == bfo.LAYOUT_PER_TENSOR:
+        # llm.c-style ZeRO-1: full-length bf16 params and grads, shard-local
+        # fp32 master/m/v for this rank's 1/N of every tensor.
+        P, M_full, _, _ = W.init_state(torch, w, 0, w.n, dev)
+        gi = torch.from_numpy(T.global_index().astype("int64")).to(dev)
+        M = M_full[gi].clone()
+        del M_full, gi
+        m = torch.zeros(S, dtype=torch.float32, device=dev)
+        v = torch.zeros(S, dtype=torch.float32, device=dev)
+        b, e = 0, S
+        g_len, g_begin = w.n, 0
+    else:
+        # Contiguous ZeRO-1 layout: full-length bf16 params, shard-local rest.
+        b, e = T.begin, T.end
+        P_full = torch.empty(w.n if w.world > 1 else 0, dtype=torch.bfloat16, device=dev)
+        P, M, m, v = W.init_state(torch, w, b, e, dev)
+        if w.world > 1:
+            P_full[b:e] = P
+            del P
+            P = P_full[b:e]
+        g_len, g_begin = S, b
     pool = []
     for k in range(max(1, args.grad_pool)):
-        G = torch.empty(S, dtype=torch.bfloat16, device=dev)
-        W.fill_grads(torch, w, G, b, k + 1)
+        G = torch.empty(g_len, dtype=torch.bfloat16, device=dev)
+        W.fill_grads(torch, w, G, g_begin, k + 1)
         pool.append(G)
     res = bfo.new_norm_result(dev)
     hp = bfo.AdamwHParams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
@@ -158,7 +179,7 @@ def main():
     gparams = S / (ms_step * 1e-3) / 1e9
     step_gbs = (UPDATE_BYTES + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
     achieved = UPDATE_BYTES * S / (upd_avg * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name) if (args.layout == "flat" and not args.pad) else None
     sumsq, norm, scale = bfo.read_norm_result(res)
 
     out = {
@@ -174,7 +195,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "n_total": w.n, "shard": [b, e], "shard_elems": S,
+        "config": {"workload": w.name + (f"+pad{args.pad}" if args.pad else ""), "n_total": w.n,
+                   "layout": args.layout, "shard": [b, e], "shard_elems": S,
                    "world": w.world, "rank": w.rank, "tensors": len(w.tensors),
                    "grad_pool": len(pool), "bytes_per_param_step": UPDATE_BYTES + NORM_BYTES},
         "hbm_gbs_step": round(step_gbs, 1),
@@ -194,7 +216,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
         del src, dst
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.layout == "flat":
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
         out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds)
     print(json.dumps(out), flush=True)

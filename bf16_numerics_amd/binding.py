@@ -24,9 +24,12 @@ EDEVICE = -7
 ROUND_SR = 0
 ROUND_RNE = 1
 FLAG_DECAY = 1
+LAYOUT_FLAT = 0
+LAYOUT_PER_TENSOR = 1
 
 # Symbols declared in include/bf16opt.h.
-EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_destroy", "bfo_table_info",
+EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_table_destroy",
+           "bfo_table_info", "bfo_table_runs",
            "grad_global_norm", "adamw_sr_step", "master_to_bf16_sr", "bfo_rng_dump",
            "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error")
 
@@ -34,6 +37,11 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_destroy", "bfo_table_in
 class BfoTensor(ctypes.Structure):
     _fields_ = [("offset", ctypes.c_uint64), ("numel", ctypes.c_uint64),
                 ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class BfoRun(ctypes.Structure):
+    _fields_ = [("local", ctypes.c_uint64), ("addr", ctypes.c_uint64), ("global_", ctypes.c_uint64),
+                ("length", ctypes.c_uint64), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class AdamwHParams(ctypes.Structure):
@@ -70,6 +78,8 @@ def _lib():
     sig = {
         "shard_range": (i32, [u64, u32, u32, pu64, pu64]),
         "bfo_table_create": (i32, [ctypes.POINTER(BfoTensor), u32, u32, u32, ctypes.POINTER(vp)]),
+        "bfo_table_create_layout": (i32, [ctypes.POINTER(BfoTensor), u32, u32, u32, i32, ctypes.POINTER(vp)]),
+        "bfo_table_runs": (i32, [vp, ctypes.POINTER(BfoRun), u32, ctypes.POINTER(u32)]),
         "bfo_table_destroy": (i32, [vp]),
         "bfo_table_info": (i32, [vp, pu64, pu64, pu64]),
         "grad_global_norm": (i32, [vp, vp, ctypes.c_float, vp, vp]),
@@ -135,13 +145,16 @@ def shard_range_status(n, world, rank):
 
 
 class Table:
-    """A validated tensor table intersected with one ZeRO-1 shard (device-resident lookup).
+    """A validated tensor table intersected with one ZeRO-1 shard (device-resident plan).
 
     entries: (offset, numel, flags) triples in buffer order; flags bit 0 = decay.
+    layout: LAYOUT_FLAT (contiguous range [begin, end); params/grads passed as
+    shard-local arrays) or LAYOUT_PER_TENSOR (1/world of every tensor;
+    params/grads passed as the full n-element buffers).
     Created on the current device; every call must use that device.
     """
 
-    def __init__(self, entries, world=1, rank=0, device=None):
+    def __init__(self, entries, world=1, rank=0, device=None, layout=LAYOUT_FLAT):
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else
                                    torch.device(device).index or 0)
         arr = (BfoTensor * max(1, len(entries)))()
@@ -149,22 +162,45 @@ class Table:
             arr[k].offset, arr[k].numel, arr[k].flags, arr[k].reserved = off, numel, flags, 0
         h = ctypes.c_void_p(None)
         with torch.cuda.device(self.device):
-            _check("bfo_table_create", _lib().bfo_table_create(arr, len(entries), world, rank, ctypes.byref(h)))
+            _check("bfo_table_create_layout",
+                   _lib().bfo_table_create_layout(arr, len(entries), world, rank, layout, ctypes.byref(h)))
         self._h = h
         n, b, e = ctypes.c_uint64(0), ctypes.c_uint64(0), ctypes.c_uint64(0)
         _check("bfo_table_info", _lib().bfo_table_info(h, ctypes.byref(n), ctypes.byref(b), ctypes.byref(e)))
         self.n, self.begin, self.end = n.value, b.value, e.value
-        self.world, self.rank = world, rank
+        self.world, self.rank, self.layout = world, rank, layout
 
     @property
     def size(self):
+        """Shard length S (elements of master / m / v)."""
         return self.end - self.begin
+
+    @property
+    def pg_size(self):
+        """Elements the params / grads arrays must hold for this layout."""
+        return self.n if self.layout == LAYOUT_PER_TENSOR else self.size
 
     @property
     def handle(self):
         if self._h is None:
             raise ValueError("table destroyed")
         return self._h
+
+    def runs(self):
+        """The shard plan: list of (local, addr, global, length, flags)."""
+        cnt = ctypes.c_uint32(0)
+        _check("bfo_table_runs", _lib().bfo_table_runs(self.handle, None, 0, ctypes.byref(cnt)))
+        arr = (BfoRun * max(1, cnt.value))()
+        _check("bfo_table_runs", _lib().bfo_table_runs(self.handle, arr, cnt.value, ctypes.byref(cnt)))
+        return [(r.local, r.addr, r.global_, r.length, r.flags) for r in arr[:cnt.value]]
+
+    def global_index(self):
+        """Global index of every shard position, expanded from the plan (numpy uint64)."""
+        import numpy as np
+        out = np.empty(self.size, np.uint64)
+        for local, _addr, glob, length, _flags in self.runs():
+            out[local:local + length] = np.arange(glob, glob + length, dtype=np.uint64)
+        return out
 
     def close(self):
         if getattr(self, "_h", None) is not None:
@@ -199,7 +235,7 @@ def scale_ptr(res):
 
 def grad_global_norm(table, grads, out, max_norm=1.0):
     dev = table.device
-    g = _arg(grads, torch.bfloat16, table.size, "grads", dev)
+    g = _arg(grads, torch.bfloat16, table.pg_size, "grads", dev)
     if out.dtype != torch.float64 or out.numel() != 2 or out.device != dev:
         raise ValueError("out must be new_norm_result(device)")
     with torch.cuda.device(dev):
@@ -214,8 +250,8 @@ def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
     (its .scale is used), an int device address, or None for 1.0."""
     dev = table.device
     S = table.size
-    p = _arg(params, torch.bfloat16, S, "params", dev)
-    g = _arg(grads, torch.bfloat16, S, "grads", dev)
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
+    g = _arg(grads, torch.bfloat16, table.pg_size, "grads", dev)
     M = _arg(master, torch.float32, S, "master", dev)
     mm = _arg(m, torch.float32, S, "m", dev)
     vv = _arg(v, torch.float32, S, "v", dev)
@@ -237,7 +273,7 @@ def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
 def master_to_bf16_sr(table, master, params, seed):
     dev = table.device
     M = _arg(master, torch.float32, table.size, "master", dev)
-    p = _arg(params, torch.bfloat16, table.size, "params", dev)
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
     with torch.cuda.device(dev):
         _check("master_to_bf16_sr", _lib().master_to_bf16_sr(table.handle, M, p, seed, _stream(dev)))
 

@@ -1,6 +1,7 @@
 // bfo_abi.cpp -- host side of the C ABI declared in include/bf16opt.h:
-// argument checks, ZeRO-1 shard arithmetic, the per-table decay lookup
-// (built and uploaded once) and the kernel launches on the caller's stream.
+// argument checks, ZeRO-1 shard arithmetic, the per-table shard plan (runs
+// and tile words, built and uploaded once) and the kernel launches on the
+// caller's stream.
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
@@ -20,23 +21,25 @@ int hipFail(hipError_t e) {
     return BFO_EHIP;
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool alignedTo(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
 
 struct bfo_table_s {
-    uint64_t n = 0, begin = 0, end = 0;
+    uint64_t n = 0, S = 0, begin = 0;
     uint32_t world = 1, rank = 0;
+    int layout = BFO_LAYOUT_FLAT;
     int device = 0;
-    uint64_t nseg = 0, ntiles = 0;
+    std::vector<bfo_run> runs;       // host copy of the plan
     void *devBlock = nullptr;        // one allocation holding everything below
     uint32_t *tile = nullptr;        // [ntiles]
-    uint64_t *segStart = nullptr;    // [nseg + 1], last = UINT64_MAX
-    uint8_t *segFlag = nullptr;      // [nseg]
-    double *normPartials = nullptr;  // [normTiles(S / 8) + normRuns(...)], at least 1
+    uint64_t *local = nullptr;       // [nruns + 1], last = UINT64_MAX
+    uint64_t *addr = nullptr;        // [nruns]
+    uint64_t *rng = nullptr;         // [nruns]
+    uint8_t *flag = nullptr;         // [nruns]
+    double *normPartials = nullptr;  // [normTiles(S) + normRuns(...)], at least 1
 
-    uint64_t S() const { return end - begin; }
-    bfo::DecayView view() const { return {tile, segStart, segFlag}; }
+    bfo::ShardView view() const { return {tile, local, addr, rng, flag}; }
 };
 
 extern "C" {
@@ -52,11 +55,12 @@ int shard_range(uint64_t n, uint32_t world, uint32_t rank, uint64_t *begin, uint
     return BFO_OK;
 }
 
-int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
-                     bfo_table *out) {
+int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
+                            int layout, bfo_table *out) {
     if (!out || (count > 0 && !tensors)) return BFO_EINVAL;
     *out = nullptr;
-    if (count >= bfo::kTileMixed) return BFO_ETABLE;  // segment ids must fit in 31 bits
+    if (layout != BFO_LAYOUT_FLAT && layout != BFO_LAYOUT_PER_TENSOR) return BFO_EINVAL;
+    if (count >= bfo::kTileMixed) return BFO_ETABLE;  // run ids must fit in 31 bits
 
     // Table: contiguous from 0, known flag bits only, no overflow.
     uint64_t n = 0;
@@ -69,59 +73,90 @@ int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, 
     uint64_t b = 0, e = 0;
     int rc = shard_range(n, world, rank, &b, &e);
     if (rc != BFO_OK) return rc;
-    if (b % 8 != 0) return BFO_EMISALIGNED;
-    const uint64_t S = e - b;
 
-    // Segments: maximal runs of equal decay flag inside [b, e), shard-local.
-    std::vector<uint64_t> segStart;
-    std::vector<uint8_t> segFlag;
-    for (uint32_t k = 0; k < count; ++k) {
-        const uint64_t lo = tensors[k].offset > b ? tensors[k].offset : b;
-        const uint64_t tend = tensors[k].offset + tensors[k].numel;
-        const uint64_t hi = tend < e ? tend : e;
-        if (lo >= hi) continue;
-        const uint8_t f = uint8_t(tensors[k].flags & BFO_FLAG_DECAY);
-        if (segFlag.empty() || segFlag.back() != f) {
-            segStart.push_back(lo - b);
-            segFlag.push_back(f);
+    // Runs.  Flat: each tensor's piece of [b, e), addressed shard-locally.
+    // Per tensor: rank r's 1/world slice of every tensor, addressed in the
+    // full buffer.  Pieces that continue one another with the same flag merge.
+    std::vector<bfo_run> runs;
+    auto push = [&runs](uint64_t local, uint64_t addr, uint64_t global, uint64_t len, uint32_t flags) {
+        if (!runs.empty()) {
+            bfo_run &p = runs.back();
+            if (p.flags == flags && p.addr + p.length == addr && p.global + p.length == global) {
+                p.length += len;
+                return;
+            }
         }
+        runs.push_back(bfo_run{local, addr, global, len, flags, 0u});
+    };
+    uint64_t S = 0;
+    if (layout == BFO_LAYOUT_FLAT) {
+        for (uint32_t k = 0; k < count; ++k) {
+            const uint64_t lo = tensors[k].offset > b ? tensors[k].offset : b;
+            const uint64_t tend = tensors[k].offset + tensors[k].numel;
+            const uint64_t hi = tend < e ? tend : e;
+            if (lo >= hi) continue;
+            push(lo - b, lo - b, lo, hi - lo, tensors[k].flags & BFO_FLAG_DECAY);
+        }
+        S = e - b;
+    } else {
+        for (uint32_t k = 0; k < count; ++k)
+            if (tensors[k].numel % world != 0) return BFO_ENOTDIVISIBLE;
+        for (uint32_t k = 0; k < count; ++k) {
+            const uint64_t len = tensors[k].numel / world;
+            if (len == 0) continue;
+            const uint64_t g = tensors[k].offset + uint64_t(rank) * len;
+            push(S, g, g, len, tensors[k].flags & BFO_FLAG_DECAY);
+            S += len;
+        }
+        b = 0;
     }
-    const uint64_t nseg = segFlag.size();
-    segStart.push_back(UINT64_MAX);
+    const uint64_t nruns = runs.size();
+    std::vector<uint64_t> local(nruns + 1), addr(nruns ? nruns : 1), rng(nruns ? nruns : 1);
+    std::vector<uint8_t> flag(nruns ? nruns : 1, 0);
+    for (uint64_t k = 0; k < nruns; ++k) {
+        local[k] = runs[k].local;
+        addr[k] = runs[k].addr;
+        rng[k] = runs[k].global;
+        flag[k] = uint8_t(runs[k].flags & BFO_FLAG_DECAY);
+    }
+    local[nruns] = UINT64_MAX;
 
-    // Tile words: uniform flag, or the segment holding the tile's first element.
+    // Tile words: the run holding each tile's first element, and whether the
+    // tile runs past that run's end.
     const uint64_t ntiles = (S + bfo::kTileElems - 1) / bfo::kTileElems;
     std::vector<uint32_t> tileWord(ntiles ? ntiles : 1, 0u);
     uint64_t k = 0;
     for (uint64_t t = 0; t < ntiles; ++t) {
         const uint64_t t0 = t * bfo::kTileElems;
         const uint64_t t1 = t0 + bfo::kTileElems < S ? t0 + bfo::kTileElems : S;
-        while (segStart[k + 1] <= t0) ++k;
-        tileWord[t] = segStart[k + 1] >= t1 ? uint32_t(segFlag[k]) : (uint32_t(k) | bfo::kTileMixed);
+        while (local[k + 1] <= t0) ++k;
+        tileWord[t] = uint32_t(k) | (local[k + 1] < t1 ? bfo::kTileMixed : 0u);
     }
 
     bfo_table_s *tb = new (std::nothrow) bfo_table_s;
     if (!tb) return BFO_EINVAL;
     tb->n = n;
+    tb->S = S;
     tb->begin = b;
-    tb->end = e;
     tb->world = world;
     tb->rank = rank;
-    tb->nseg = nseg;
-    tb->ntiles = ntiles;
+    tb->layout = layout;
+    tb->runs = runs;
     hipError_t he = hipGetDevice(&tb->device);
     if (he != hipSuccess) {
         delete tb;
         return hipFail(he);
     }
-    auto up8 = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
-    const uint64_t offTile = 0;
-    const uint64_t offSeg = offTile + up8(tileWord.size() * sizeof(uint32_t));
-    const uint64_t offFlag = offSeg + up8(segStart.size() * sizeof(uint64_t));
-    const uint64_t offNorm = offFlag + up8(segFlag.size() + 1);
-    const uint64_t nTiles = bfo::normTiles(S / 8);
+    auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+    const uint64_t nTiles = bfo::normTiles(S);
     const uint64_t nNorm = nTiles + bfo::normRuns(nTiles) > 0 ? nTiles + bfo::normRuns(nTiles) : 1;
-    const uint64_t bytes = offNorm + up8(nNorm * sizeof(double));
+    const uint64_t offTile = 0;
+    const uint64_t offLocal = offTile + up(tileWord.size() * sizeof(uint32_t));
+    const uint64_t offAddr = offLocal + up(local.size() * sizeof(uint64_t));
+    const uint64_t offRng = offAddr + up(addr.size() * sizeof(uint64_t));
+    const uint64_t offFlag = offRng + up(rng.size() * sizeof(uint64_t));
+    const uint64_t offNorm = offFlag + up(flag.size());
+    const uint64_t bytes = offNorm + up(nNorm * sizeof(double));
     he = hipMalloc(&tb->devBlock, bytes);
     if (he != hipSuccess) {
         delete tb;
@@ -129,22 +164,31 @@ int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, 
     }
     char *base = static_cast<char *>(tb->devBlock);
     tb->tile = reinterpret_cast<uint32_t *>(base + offTile);
-    tb->segStart = reinterpret_cast<uint64_t *>(base + offSeg);
-    tb->segFlag = reinterpret_cast<uint8_t *>(base + offFlag);
+    tb->local = reinterpret_cast<uint64_t *>(base + offLocal);
+    tb->addr = reinterpret_cast<uint64_t *>(base + offAddr);
+    tb->rng = reinterpret_cast<uint64_t *>(base + offRng);
+    tb->flag = reinterpret_cast<uint8_t *>(base + offFlag);
     tb->normPartials = reinterpret_cast<double *>(base + offNorm);
-    segFlag.push_back(0);  // keeps the copy non-empty for an empty shard
     if ((he = hipMemcpy(tb->tile, tileWord.data(), tileWord.size() * sizeof(uint32_t),
                         hipMemcpyHostToDevice)) != hipSuccess ||
-        (he = hipMemcpy(tb->segStart, segStart.data(), segStart.size() * sizeof(uint64_t),
-                        hipMemcpyHostToDevice)) != hipSuccess ||
-        (he = hipMemcpy(tb->segFlag, segFlag.data(), segFlag.size(), hipMemcpyHostToDevice)) !=
-            hipSuccess) {
+        (he = hipMemcpy(tb->local, local.data(), local.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) !=
+            hipSuccess ||
+        (he = hipMemcpy(tb->addr, addr.data(), addr.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) !=
+            hipSuccess ||
+        (he = hipMemcpy(tb->rng, rng.data(), rng.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) !=
+            hipSuccess ||
+        (he = hipMemcpy(tb->flag, flag.data(), flag.size(), hipMemcpyHostToDevice)) != hipSuccess) {
         (void)hipFree(tb->devBlock);
         delete tb;
         return hipFail(he);
     }
     *out = tb;
     return BFO_OK;
+}
+
+int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
+                     bfo_table *out) {
+    return bfo_table_create_layout(tensors, count, world, rank, BFO_LAYOUT_FLAT, out);
 }
 
 int bfo_table_destroy(bfo_table table) {
@@ -158,7 +202,17 @@ int bfo_table_info(bfo_table table, uint64_t *n, uint64_t *begin, uint64_t *end)
     if (!table) return BFO_EINVAL;
     if (n) *n = table->n;
     if (begin) *begin = table->begin;
-    if (end) *end = table->end;
+    if (end) *end = table->begin + table->S;
+    return BFO_OK;
+}
+
+int bfo_table_runs(bfo_table table, bfo_run *out, uint32_t capacity, uint32_t *count) {
+    if (!table || !count) return BFO_EINVAL;
+    *count = uint32_t(table->runs.size());
+    if (out) {
+        if (capacity < table->runs.size()) return BFO_ERANGE;
+        std::memcpy(out, table->runs.data(), table->runs.size() * sizeof(bfo_run));
+    }
     return BFO_OK;
 }
 
@@ -179,12 +233,12 @@ extern "C" {
 
 int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
                      void *stream) {
-    if (!table || !out || (table->S() && !grads)) return BFO_EINVAL;
-    if (!aligned16(grads) || !aligned16(out)) return BFO_EMISALIGNED;
+    if (!table || !out || (table->S && !grads)) return BFO_EINVAL;
+    if (!alignedTo(grads, 2) || !alignedTo(out, 16)) return BFO_EMISALIGNED;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
-    hipError_t he = bfo::launchNorm(grads, table->S(), max_norm, table->normPartials, out,
-                                    static_cast<hipStream_t>(stream));
+    hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0, max_norm,
+                                    table->normPartials, out, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
@@ -193,10 +247,10 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
                   uint64_t seed, int rounding, void *stream) {
     if (!table || !hp || t == 0) return BFO_EINVAL;
     if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
-    const uint64_t S = table->S();
+    const uint64_t S = table->S;
     if (S && (!params || !grads || !m || !v)) return BFO_EINVAL;
-    if (!aligned16(params) || !aligned16(grads) || !aligned16(master) || !aligned16(m) ||
-        !aligned16(v) || (reinterpret_cast<uintptr_t>(scale) & 3u))
+    if (!alignedTo(params, 2) || !alignedTo(grads, 2) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
+        !alignedTo(v, 16) || !alignedTo(scale, 4))
         return BFO_EMISALIGNED;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
@@ -213,39 +267,39 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
     s.bc1 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta1), double(t))) : 1.0f;
     s.bc2 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta2), double(t))) : 1.0f;
 
-    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), s, scale,
-                                     table->begin / 8, seed, rounding,
-                                     static_cast<hipStream_t>(stream));
+    const int pgVec = alignedTo(params, 16) && alignedTo(grads, 16) ? 1 : 0;
+    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, scale, seed,
+                                     rounding, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
 int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
                       void *stream) {
     if (!table) return BFO_EINVAL;
-    const uint64_t S = table->S();
+    const uint64_t S = table->S;
     if (S && (!master || !params)) return BFO_EINVAL;
-    if (!aligned16(master) || !aligned16(params)) return BFO_EMISALIGNED;
+    if (!alignedTo(master, 16) || !alignedTo(params, 2)) return BFO_EMISALIGNED;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
     if (S == 0) return BFO_OK;
-    hipError_t he = bfo::launchMasterToBf16(master, params, S, table->begin / 8, seed,
-                                            static_cast<hipStream_t>(stream));
+    hipError_t he = bfo::launchMasterToBf16(master, params, S, table->view(), alignedTo(params, 16) ? 1 : 0,
+                                            seed, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
 int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, void *stream) {
     if (count && !out) return BFO_EINVAL;
-    if (reinterpret_cast<uintptr_t>(out) & 1u) return BFO_EMISALIGNED;
+    if (!alignedTo(out, 2)) return BFO_EMISALIGNED;
     if (count > UINT64_MAX - first) return BFO_ERANGE;
     hipError_t he = bfo::launchRngDump(first, count, seed, out, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
 int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream) {
-    if (!table || (table->S() && !out)) return BFO_EINVAL;
+    if (!table || (table->S && !out)) return BFO_EINVAL;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
-    hipError_t he = bfo::launchDecayDump(table->view(), table->S(), out, static_cast<hipStream_t>(stream));
+    hipError_t he = bfo::launchDecayDump(table->view(), table->S, out, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
@@ -253,9 +307,9 @@ const char *bfo_status_string(int status) {
     switch (status) {
         case BFO_OK: return "ok";
         case BFO_EINVAL: return "invalid argument";
-        case BFO_ENOTDIVISIBLE: return "buffer length not divisible by the shard count";
+        case BFO_ENOTDIVISIBLE: return "length not divisible by the shard count";
         case BFO_ERANGE: return "rank or range out of bounds";
-        case BFO_EMISALIGNED: return "pointer not 16-byte aligned or shard start not a multiple of 8";
+        case BFO_EMISALIGNED: return "pointer not aligned as required";
         case BFO_ETABLE: return "tensor table not contiguous from 0 or undefined flag bits";
         case BFO_EHIP: return "HIP runtime call failed";
         case BFO_EDEVICE: return "current device differs from the table's device";

@@ -16,14 +16,14 @@ constexpr int kBlock = 256;
 constexpr int kVecPerLane = 2;
 constexpr uint64_t kTileVecs = uint64_t(kBlock) * kVecPerLane;  // vectors per workgroup
 constexpr uint64_t kTileElems = kTileVecs * 8;                  // elements per workgroup
-// Decay lookup: one 32-bit word per tile.  Bit 31 clear: every element of
-// the tile has the same flag, held in bit 0.  Bit 31 set: the tile crosses a
-// flag change; bits 0..30 give the segment holding the tile's first element.
+// Shard lookup: one 32-bit word per tile.  Bits 0..30 give the run that
+// holds the tile's first element; bit 31 is set when the tile crosses into
+// another run (lanes then scan forward from that run).
 constexpr uint32_t kTileMixed = 0x80000000u;
 
 // Grad-norm partition: stage 1 gives each workgroup one tile of
-// kNormTileVecs vectors (kNormVecPerLane per lane, strided by the block) and
-// writes one binary64 partial per tile.  When there are more than
+// kNormTileVecs vectors (kNormVecPerLane per lane, strided by the block; the
+// last vector may be partial) and writes one binary64 partial per tile.  When there are more than
 // kNormFinishDirect tiles, an intermediate pass sums each run of
 // kNormReduceRun partials in its own workgroup; stage 2 (one workgroup) sums
 // what is left in a fixed order.  All of it depends only on the shard length.
@@ -33,35 +33,42 @@ constexpr int kNormFinishBlock = 1024;
 constexpr uint64_t kNormFinishDirect = 32768;
 constexpr uint64_t kNormReduceRun = 4096;
 
-inline uint64_t normTiles(uint64_t nvec) { return (nvec + kNormTileVecs - 1) / kNormTileVecs; }
+inline uint64_t normTiles(uint64_t S) { return ((S + 7) / 8 + kNormTileVecs - 1) / kNormTileVecs; }
 inline uint64_t normRuns(uint64_t ntiles) {
     return ntiles > kNormFinishDirect ? (ntiles + kNormReduceRun - 1) / kNormReduceRun : 0;
 }
 
-// Device view of a table's decay lookup.  Segments are maximal runs of
-// equal flag in shard-local coordinates; segStart has nseg + 1 entries, the
-// last being UINT64_MAX so scans always stop.
-struct DecayView {
+// Device view of a table's shard plan.  A run is a stretch of shard-local
+// elements [local[k], local[k+1]) that sits at consecutive positions of the
+// caller's params/grads arrays (starting at addr[k]) and of the flat buffer
+// (global index rng[k], which keys the rounding draws), with one decay flag.
+// local has nruns + 1 entries, the last being UINT64_MAX so scans stop.
+struct ShardView {
     const uint32_t *tile;
-    const uint64_t *segStart;
-    const uint8_t *segFlag;
+    const uint64_t *local;
+    const uint64_t *addr;
+    const uint64_t *rng;
+    const uint8_t *flag;
 };
 
 struct StepScalars {
     float lr, beta1, beta2, eps, wd, bc1, bc2;
 };
 
-// Launchers (bfo_kernels.hip).  Shapes are checked by the caller: every
-// pointer addresses S elements (S = shard length), 16-byte aligned.
-hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *partials,
-                      bfo_norm_result *out, hipStream_t stream);
+// Launchers (bfo_kernels.hip).  Shapes are checked by the caller: M, m, v
+// hold S shard-local elements, 16-byte aligned; P and G are addressed
+// through the runs and are at least 2-byte aligned; pgVec says whether P
+// and G are 16-byte aligned (then 8-element vectors at 8-aligned positions
+// use 16-byte accesses).
+hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, float maxNorm,
+                      double *partials, bfo_norm_result *out, hipStream_t stream);
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
-                       DecayView dv, StepScalars s, const float *scale, uint64_t group0,
-                       uint64_t seed, int rounding, hipStream_t stream);
-hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, uint64_t group0,
+                       ShardView sv, int pgVec, StepScalars s, const float *scale, uint64_t seed,
+                       int rounding, hipStream_t stream);
+hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
                               uint64_t seed, hipStream_t stream);
 hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out,
                          hipStream_t stream);
-hipError_t launchDecayDump(DecayView dv, uint64_t S, uint8_t *out, hipStream_t stream);
+hipError_t launchDecayDump(ShardView sv, uint64_t S, uint8_t *out, hipStream_t stream);
 
 }  // namespace bfo

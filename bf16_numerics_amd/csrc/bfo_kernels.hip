@@ -5,6 +5,18 @@
 // stores, several in flight per lane, and enough workgroups (>> 256 CUs) to
 // keep every channel busy.  Nothing is a contraction, so there is no MFMA.
 //
+// Shard plan.  The shard's S elements are shard-local positions j; runs map
+// them to positions in the caller's params/grads arrays (addr) and to global
+// indices of the flat buffer (rng, which keys the rounding draws).  Work is
+// cut into 8-element vectors at shard-local positions 8q:
+//   - regular: the vector lies in one run and P/G are 16-byte aligned at its
+//     address: every array moves as 16-byte accesses (the common case);
+//   - semi-regular: one run, but P/G not 16-byte aligned there (misaligned
+//     flat shards): fp32 state as 16-byte accesses, bf16 P/G per element;
+//   - per element: the vector crosses runs or the shard end.
+// A vector's draws come from one Philox block when its global index is
+// 8-aligned and from two otherwise.
+//
 // Floating point.  The update is a fixed sequence of binary32 operations
 // (one IEEE operation per line of the per-element function), built with
 // -ffp-contract=off so the compiler fuses nothing that is not written as
@@ -14,8 +26,8 @@
 //
 // Page references (title, section):
 //   "04 · 多 GPU 与混合精度": §2.2 the AdamW element update and the two-FMA
-//     lerp; §2.3 stochastic rounding; §4 grad norm and clip; §5.2 rebuilding
-//     bf16 weights from the master with the same draws.
+//     lerp; §2.3 stochastic rounding; §3.2 sharding; §4 grad norm and clip;
+//     §5.2 rebuilding bf16 weights from the master with the same draws.
 //   "第 13 讲：扩大 LLM——优化与并行训练": §1.7 bias correction and
 //     decoupled weight decay.
 //   Philox4x32-10: Salmon, Moraes, Dror, Shaw, SC'11.
@@ -29,7 +41,7 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Counter-based draws: Philox4x32-10.  One block of four 32-bit words serves
-// the aligned group of 8 elements (global index >> 3).
+// the aligned group of 8 global indices (index >> 3).
 // ---------------------------------------------------------------------------
 struct U32x4 {
     uint32_t x, y, z, w;
@@ -55,10 +67,24 @@ __device__ __forceinline__ U32x4 philox10(uint64_t group, uint32_t k0, uint32_t 
     return {c0, c1, c2, c3};
 }
 
-// 16-bit draw of element e (0..7) of a group: word e>>1, low half for even e.
-__device__ __forceinline__ uint32_t drawOf(const U32x4 &w, int e) {
-    const uint32_t word = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
-    return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+// 16-bit draw for position p (0..7) of a group: word p>>1, low half for even p.
+__device__ __forceinline__ uint32_t drawOf(const U32x4 &w, int p) {
+    const uint32_t word = (p >> 1) == 0 ? w.x : (p >> 1) == 1 ? w.y : (p >> 1) == 2 ? w.z : w.w;
+    return (p & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// Draws of the 8 consecutive global indices rng0 .. rng0+7.
+__device__ __forceinline__ void draws8(uint64_t rng0, uint32_t k0, uint32_t k1, uint32_t d[8]) {
+    const U32x4 a = philox10(rng0 >> 3, k0, k1);
+    const int s = int(rng0 & 7);
+    if (s == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = drawOf(a, e);
+    } else {
+        const U32x4 b = philox10((rng0 >> 3) + 1, k0, k1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = (s + e) < 8 ? drawOf(a, s + e) : drawOf(b, s + e - 8);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -83,21 +109,54 @@ __device__ __forceinline__ uint32_t roundRNE(float x) {
 
 __device__ __forceinline__ float bf16Lo(uint32_t word) { return __uint_as_float(word << 16); }
 __device__ __forceinline__ float bf16Hi(uint32_t word) { return __uint_as_float(word & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16At(const uint16_t *p, uint64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
+
+template <int kRound>
+__device__ __forceinline__ uint32_t writeBack(float p, uint32_t draw) {
+    if constexpr (kRound == BFO_ROUND_SR) return roundSR(p, draw);
+    else return roundRNE(p);
+}
+
+// Eight consecutive bf16 patterns from a 2-byte-aligned address, packed as in
+// a 16-byte load.
+__device__ __forceinline__ uint4 load8Narrow(const uint16_t *p) {
+    return make_uint4(uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16),
+                      uint32_t(p[4]) | (uint32_t(p[5]) << 16), uint32_t(p[6]) | (uint32_t(p[7]) << 16));
+}
 
 // ---------------------------------------------------------------------------
-// Decay flags of the 8 elements starting at shard-local j0 (bit e = element
-// j0 + e), from the tile word and, inside mixed tiles, the segment list.
+// Shard plan lookups.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t decayMask8(const DecayView &dv, uint32_t tileWord, uint64_t j0) {
-    if (!(tileWord & kTileMixed)) return (tileWord & 1u) ? 0xFFu : 0u;
+struct Place {
+    uint32_t run;   // run holding the vector's first element
+    bool inRun;     // all 8 elements exist and lie in that run
+    uint64_t addr0; // P/G position of the first element
+    uint64_t rng0;  // global index of the first element
+};
+
+__device__ __forceinline__ Place placeVector(const ShardView &sv, uint32_t tileWord, uint64_t j0, uint64_t S) {
+    Place pl;
     uint32_t k = tileWord & ~kTileMixed;
-    while (dv.segStart[k + 1] <= j0) ++k;
-    uint32_t mask = 0;
-    for (int e = 0; e < 8; ++e) {
-        while (dv.segStart[k + 1] <= j0 + uint64_t(e)) ++k;
-        mask |= uint32_t(dv.segFlag[k] & 1u) << e;
+    uint64_t runEnd = UINT64_MAX;
+    if (tileWord & kTileMixed) {
+        while (sv.local[k + 1] <= j0) ++k;
+        runEnd = sv.local[k + 1];
     }
-    return mask;
+    pl.run = k;
+    pl.inRun = j0 + 8 <= S && j0 + 8 <= runEnd;
+    const uint64_t off = j0 - sv.local[k];
+    pl.addr0 = sv.addr[k] + off;
+    pl.rng0 = sv.rng[k] + off;
+    return pl;
+}
+
+// Element j: advances k to its run, returns its P/G position and global index.
+__device__ __forceinline__ void placeElement(const ShardView &sv, uint32_t &k, uint64_t j, uint64_t &addr,
+                                             uint64_t &rng) {
+    while (sv.local[k + 1] <= j) ++k;
+    const uint64_t off = j - sv.local[k];
+    addr = sv.addr[k] + off;
+    rng = sv.rng[k] + off;
 }
 
 // ---------------------------------------------------------------------------
@@ -122,61 +181,101 @@ __device__ __forceinline__ float adamwElem(float graw, float &m, float &v, float
     return old - q;
 }
 
-template <int kRound>
-__device__ __forceinline__ uint32_t writeBack(float p, const U32x4 &draws, int e) {
-    if constexpr (kRound == BFO_ROUND_SR) return roundSR(p, drawOf(draws, e));
-    else return roundRNE(p);
+enum : int { kNone = 0, kRegular = 1, kSemi = 2, kPerElement = 3 };
+
+// Per-element path of the update: the vector crosses runs or the shard end.
+template <bool kMaster, int kRound>
+__device__ void adamwElementwise(uint16_t *P, const uint16_t *G, float *M, float *Mom, float *Var, uint64_t j0,
+                                 uint64_t S, const ShardView &sv, uint32_t run, const StepScalars &s,
+                                 float scale, uint32_t key0, uint32_t key1) {
+    uint32_t k = run;
+    uint64_t cachedGroup = UINT64_MAX;
+    U32x4 cached{0u, 0u, 0u, 0u};
+    for (int e = 0; e < 8; ++e) {
+        const uint64_t j = j0 + uint64_t(e);
+        if (j >= S) break;
+        uint64_t addr, rng;
+        placeElement(sv, k, j, addr, rng);
+        const float w = sv.flag[k] ? s.wd : 0.0f;
+        uint32_t draw = 0;
+        if constexpr (kRound == BFO_ROUND_SR) {
+            if ((rng >> 3) != cachedGroup) {
+                cachedGroup = rng >> 3;
+                cached = philox10(cachedGroup, key0, key1);
+            }
+            draw = drawOf(cached, int(rng & 7));
+        }
+        float mm = Mom[j], vv = Var[j];
+        const float old = kMaster ? M[j] : bf16At(P, addr);
+        const float p = adamwElem(bf16At(G, addr), mm, vv, old, w, s, scale);
+        Mom[j] = mm;
+        Var[j] = vv;
+        if constexpr (kMaster) M[j] = p;
+        P[addr] = uint16_t(writeBack<kRound>(p, draw));
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Fused update over full 8-element vectors.  Workgroup `tile` owns vectors
+// Fused update.  Workgroup `tile` owns shard-local vectors
 // [tile * kTileVecs, +kTileVecs); lane t takes vectors t and t + 256 of it,
 // so each load instruction of a wave covers 1 KiB (bf16) or 2 KiB (fp32) of
-// contiguous memory.  All loads of a lane are issued before any math.
+// contiguous memory.  All loads of the run-aligned vectors are issued before
+// any math.
 // ---------------------------------------------------------------------------
 template <bool kMaster, int kRound>
 __global__ __launch_bounds__(kBlock) void adamwTileKernel(
     uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
-    float *__restrict__ Mom, float *__restrict__ Var, uint64_t nvec, DecayView dv, StepScalars s,
-    const float *__restrict__ scalePtr, uint64_t group0, uint32_t key0, uint32_t key1,
-    uint64_t tileBase) {
+    float *__restrict__ Mom, float *__restrict__ Var, uint64_t S, ShardView sv, int pgVec, StepScalars s,
+    const float *__restrict__ scalePtr, uint32_t key0, uint32_t key1, uint64_t tileBase) {
     const float scale = scalePtr ? *scalePtr : 1.0f;
     const uint64_t tile = tileBase + blockIdx.x;
-    const uint32_t tileWord = dv.tile[tile];
+    const uint32_t tileWord = sv.tile[tile];
 
     uint4 gv[kVecPerLane], pv[kVecPerLane];
     float4 ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
     float4 wa[kVecPerLane], wb[kVecPerLane];
-    uint64_t qv[kVecPerLane];
-    bool ok[kVecPerLane];
+    Place pl[kVecPerLane];
+    int mode[kVecPerLane];
 
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
-        qv[k] = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-        ok[k] = qv[k] < nvec;
-        if (ok[k]) {
-            const uint64_t q = qv[k];
-            gv[k] = reinterpret_cast<const uint4 *>(G)[q];
-            ma[k] = reinterpret_cast<const float4 *>(Mom)[2 * q];
-            mb[k] = reinterpret_cast<const float4 *>(Mom)[2 * q + 1];
-            va[k] = reinterpret_cast<const float4 *>(Var)[2 * q];
-            vb[k] = reinterpret_cast<const float4 *>(Var)[2 * q + 1];
-            if constexpr (kMaster) {
-                wa[k] = reinterpret_cast<const float4 *>(M)[2 * q];
-                wb[k] = reinterpret_cast<const float4 *>(M)[2 * q + 1];
-            } else {
-                pv[k] = reinterpret_cast<const uint4 *>(P)[q];
-            }
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        mode[k] = kNone;
+        if (q * 8 >= S) continue;
+        pl[k] = placeVector(sv, tileWord, q * 8, S);
+        if (!pl[k].inRun) {
+            mode[k] = kPerElement;
+            continue;
+        }
+        mode[k] = (pgVec && (pl[k].addr0 & 7) == 0) ? kRegular : kSemi;
+        ma[k] = reinterpret_cast<const float4 *>(Mom)[2 * q];
+        mb[k] = reinterpret_cast<const float4 *>(Mom)[2 * q + 1];
+        va[k] = reinterpret_cast<const float4 *>(Var)[2 * q];
+        vb[k] = reinterpret_cast<const float4 *>(Var)[2 * q + 1];
+        if constexpr (kMaster) {
+            wa[k] = reinterpret_cast<const float4 *>(M)[2 * q];
+            wb[k] = reinterpret_cast<const float4 *>(M)[2 * q + 1];
+        }
+        if (mode[k] == kRegular) {
+            gv[k] = reinterpret_cast<const uint4 *>(G)[pl[k].addr0 >> 3];
+            if constexpr (!kMaster) pv[k] = reinterpret_cast<const uint4 *>(P)[pl[k].addr0 >> 3];
+        } else {
+            gv[k] = load8Narrow(G + pl[k].addr0);
+            if constexpr (!kMaster) pv[k] = load8Narrow(P + pl[k].addr0);
         }
     }
 
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
-        if (!ok[k]) continue;
-        const uint64_t q = qv[k];
-        U32x4 draws{0u, 0u, 0u, 0u};
-        if constexpr (kRound == BFO_ROUND_SR) draws = philox10(group0 + q, key0, key1);
-        const uint32_t dmask = decayMask8(dv, tileWord, q * 8);
+        if (mode[k] == kNone) continue;
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (mode[k] == kPerElement) {
+            adamwElementwise<kMaster, kRound>(P, G, M, Mom, Var, q * 8, S, sv, pl[k].run, s, scale, key0, key1);
+            continue;
+        }
+        uint32_t draws[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if constexpr (kRound == BFO_ROUND_SR) draws8(pl[k].rng0, key0, key1, draws);
+        const float w = sv.flag[pl[k].run] ? s.wd : 0.0f;
 
         float gr[8] = {bf16Lo(gv[k].x), bf16Hi(gv[k].x), bf16Lo(gv[k].y), bf16Hi(gv[k].y),
                        bf16Lo(gv[k].z), bf16Hi(gv[k].z), bf16Lo(gv[k].w), bf16Hi(gv[k].w)};
@@ -196,9 +295,8 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
         uint32_t hb[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float w = ((dmask >> e) & 1u) ? s.wd : 0.0f;
             pn[e] = adamwElem(gr[e], mm[e], vv[e], old[e], w, s, scale);
-            hb[e] = writeBack<kRound>(pn[e], draws, e);
+            hb[e] = writeBack<kRound>(pn[e], draws[e]);
         }
         reinterpret_cast<float4 *>(Mom)[2 * q] = make_float4(mm[0], mm[1], mm[2], mm[3]);
         reinterpret_cast<float4 *>(Mom)[2 * q + 1] = make_float4(mm[4], mm[5], mm[6], mm[7]);
@@ -208,91 +306,96 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
             reinterpret_cast<float4 *>(M)[2 * q] = make_float4(pn[0], pn[1], pn[2], pn[3]);
             reinterpret_cast<float4 *>(M)[2 * q + 1] = make_float4(pn[4], pn[5], pn[6], pn[7]);
         }
-        uint4 out;
-        out.x = hb[0] | (hb[1] << 16);
-        out.y = hb[2] | (hb[3] << 16);
-        out.z = hb[4] | (hb[5] << 16);
-        out.w = hb[6] | (hb[7] << 16);
-        reinterpret_cast<uint4 *>(P)[q] = out;
-    }
-}
-
-// The last S % 8 elements (at most 7), one lane each, with scalar accesses.
-template <bool kMaster, int kRound>
-__global__ __launch_bounds__(64) void adamwTailKernel(uint16_t *P, const uint16_t *G, float *M,
-                                                      float *Mom, float *Var, uint64_t j0,
-                                                      uint32_t count, DecayView dv, StepScalars s,
-                                                      const float *scalePtr, uint64_t group,
-                                                      uint32_t key0, uint32_t key1) {
-    const int e = int(threadIdx.x);
-    if (e >= int(count)) return;
-    const uint64_t j = j0 + uint64_t(e);
-    const float scale = scalePtr ? *scalePtr : 1.0f;
-    const uint32_t dmask = decayMask8(dv, dv.tile[j0 / kTileElems], j0);
-    U32x4 draws{0u, 0u, 0u, 0u};
-    if constexpr (kRound == BFO_ROUND_SR) draws = philox10(group, key0, key1);
-    float mm = Mom[j], vv = Var[j];
-    const float old = kMaster ? M[j] : __uint_as_float(uint32_t(P[j]) << 16);
-    const float w = ((dmask >> e) & 1u) ? s.wd : 0.0f;
-    const float p = adamwElem(__uint_as_float(uint32_t(G[j]) << 16), mm, vv, old, w, s, scale);
-    Mom[j] = mm;
-    Var[j] = vv;
-    if constexpr (kMaster) M[j] = p;
-    P[j] = uint16_t(writeBack<kRound>(p, draws, e));
-}
-
-// ---------------------------------------------------------------------------
-// Rebuild bf16 weights from the master: P = SR(M, draw).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
-                                                             uint16_t *__restrict__ P, uint64_t nvec,
-                                                             uint64_t group0, uint32_t key0,
-                                                             uint32_t key1, uint64_t tileBase) {
-    float4 a[kVecPerLane], b[kVecPerLane];
-    uint64_t qv[kVecPerLane];
-    bool ok[kVecPerLane];
+        if (mode[k] == kRegular) {
+            uint4 out;
+            out.x = hb[0] | (hb[1] << 16);
+            out.y = hb[2] | (hb[3] << 16);
+            out.z = hb[4] | (hb[5] << 16);
+            out.w = hb[6] | (hb[7] << 16);
+            reinterpret_cast<uint4 *>(P)[pl[k].addr0 >> 3] = out;
+        } else {
+            uint16_t *p = P + pl[k].addr0;
 #pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-        qv[k] = (tileBase + blockIdx.x) * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-        ok[k] = qv[k] < nvec;
-        if (ok[k]) {
-            a[k] = reinterpret_cast<const float4 *>(M)[2 * qv[k]];
-            b[k] = reinterpret_cast<const float4 *>(M)[2 * qv[k] + 1];
+            for (int e = 0; e < 8; ++e) p[e] = uint16_t(hb[e]);
         }
     }
-#pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-        if (!ok[k]) continue;
-        const U32x4 d = philox10(group0 + qv[k], key0, key1);
-        uint4 out;
-        out.x = roundSR(a[k].x, drawOf(d, 0)) | (roundSR(a[k].y, drawOf(d, 1)) << 16);
-        out.y = roundSR(a[k].z, drawOf(d, 2)) | (roundSR(a[k].w, drawOf(d, 3)) << 16);
-        out.z = roundSR(b[k].x, drawOf(d, 4)) | (roundSR(b[k].y, drawOf(d, 5)) << 16);
-        out.w = roundSR(b[k].z, drawOf(d, 6)) | (roundSR(b[k].w, drawOf(d, 7)) << 16);
-        reinterpret_cast<uint4 *>(P)[qv[k]] = out;
-    }
-}
-
-__global__ __launch_bounds__(64) void masterToBf16TailKernel(const float *M, uint16_t *P,
-                                                             uint64_t j0, uint32_t count,
-                                                             uint64_t group, uint32_t key0,
-                                                             uint32_t key1) {
-    const int e = int(threadIdx.x);
-    if (e >= int(count)) return;
-    const U32x4 d = philox10(group, key0, key1);
-    P[j0 + e] = uint16_t(roundSR(M[j0 + e], drawOf(d, e)));
 }
 
 // ---------------------------------------------------------------------------
-// Grad norm.  Stage 1: workgroup b owns vectors [b*1024, (b+1)*1024); lane t
-// loads vectors t, t+256, t+512, t+768 (four 16-byte loads in flight), sums
-// their squares in binary64 in that order, and the 256 lanes are reduced in a
-// fixed tree (wave64 butterfly, then the 4 waves through LDS) into one
-// partial per tile.  Large shards (more than kNormFinishDirect tiles) add an
-// intermediate pass: workgroup r sums partials [r*4096, (r+1)*4096) (lane t
-// takes t, t+256, ... in order, then the fixed tree).  Stage 2: one 1024-lane
-// workgroup adds the remaining partials (lane t takes t, t+1024, ... in
-// order), then the ragged tail, in a fixed tree, and derives norm and scale.
+// Rebuild bf16 weights from the master: P = SR(M, draw), same vector plan.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
+                                                             uint16_t *__restrict__ P, uint64_t S,
+                                                             ShardView sv, int pgVec, uint32_t key0,
+                                                             uint32_t key1, uint64_t tileBase) {
+    const uint64_t tile = tileBase + blockIdx.x;
+    const uint32_t tileWord = sv.tile[tile];
+    float4 a[kVecPerLane], b[kVecPerLane];
+    Place pl[kVecPerLane];
+    int mode[kVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        mode[k] = kNone;
+        if (q * 8 >= S) continue;
+        pl[k] = placeVector(sv, tileWord, q * 8, S);
+        if (!pl[k].inRun) {
+            mode[k] = kPerElement;
+            continue;
+        }
+        mode[k] = (pgVec && (pl[k].addr0 & 7) == 0) ? kRegular : kSemi;
+        a[k] = reinterpret_cast<const float4 *>(M)[2 * q];
+        b[k] = reinterpret_cast<const float4 *>(M)[2 * q + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        if (mode[k] == kNone) continue;
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (mode[k] == kPerElement) {
+            uint32_t run = pl[k].run;
+            uint64_t cachedGroup = UINT64_MAX;
+            U32x4 cached{0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e) {
+                const uint64_t j = q * 8 + uint64_t(e);
+                if (j >= S) break;
+                uint64_t addr, rng;
+                placeElement(sv, run, j, addr, rng);
+                if ((rng >> 3) != cachedGroup) {
+                    cachedGroup = rng >> 3;
+                    cached = philox10(cachedGroup, key0, key1);
+                }
+                P[addr] = uint16_t(roundSR(M[j], drawOf(cached, int(rng & 7))));
+            }
+            continue;
+        }
+        uint32_t d[8];
+        draws8(pl[k].rng0, key0, key1, d);
+        const uint32_t h0 = roundSR(a[k].x, d[0]), h1 = roundSR(a[k].y, d[1]);
+        const uint32_t h2 = roundSR(a[k].z, d[2]), h3 = roundSR(a[k].w, d[3]);
+        const uint32_t h4 = roundSR(b[k].x, d[4]), h5 = roundSR(b[k].y, d[5]);
+        const uint32_t h6 = roundSR(b[k].z, d[6]), h7 = roundSR(b[k].w, d[7]);
+        if (mode[k] == kRegular) {
+            reinterpret_cast<uint4 *>(P)[pl[k].addr0 >> 3] =
+                make_uint4(h0 | (h1 << 16), h2 | (h3 << 16), h4 | (h5 << 16), h6 | (h7 << 16));
+        } else {
+            uint16_t *p = P + pl[k].addr0;
+            p[0] = uint16_t(h0); p[1] = uint16_t(h1); p[2] = uint16_t(h2); p[3] = uint16_t(h3);
+            p[4] = uint16_t(h4); p[5] = uint16_t(h5); p[6] = uint16_t(h6); p[7] = uint16_t(h7);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grad norm.  Stage 1: workgroup b owns shard-local vectors
+// [b*1024, (b+1)*1024); lane t takes vectors t, t+256, t+512, t+768 (four
+// 16-byte loads in flight on the regular path), sums their squares in
+// binary64 in element order, and the 256 lanes are reduced in a fixed tree
+// (wave64 butterfly, then the 4 waves through LDS) into one partial per tile.
+// Large shards (more than kNormFinishDirect tiles) add an intermediate pass:
+// workgroup r sums partials [r*4096, (r+1)*4096) (lane t takes t, t+256, ...
+// in order, then the fixed tree).  Stage 2: one 1024-lane workgroup adds the
+// remaining partials (lane t takes t, t+1024, ... in order) in a fixed tree
+// and derives norm and scale.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double sumSquares8(double acc, const uint4 &x) {
     const double d0 = double(bf16Lo(x.x)), d1 = double(bf16Hi(x.x));
@@ -328,21 +431,47 @@ __device__ __forceinline__ double blockSum(double x) {
     return total;
 }
 
-__global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G,
-                                                           uint64_t nvec, double *__restrict__ partials,
-                                                           uint64_t tileBase) {
-    const uint4 *g = reinterpret_cast<const uint4 *>(G);
+__global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G, uint64_t S,
+                                                           ShardView sv, int pgVec,
+                                                           double *__restrict__ partials, uint64_t tileBase) {
     const uint64_t tile = tileBase + blockIdx.x;
-    const uint64_t base = tile * kNormTileVecs + threadIdx.x;
     uint4 x[kNormVecPerLane];
+    Place pl[kNormVecPerLane];
+    int mode[kNormVecPerLane];
 #pragma unroll
     for (int k = 0; k < kNormVecPerLane; ++k) {
-        const uint64_t q = base + uint64_t(k) * kBlock;
-        x[k] = q < nvec ? g[q] : make_uint4(0u, 0u, 0u, 0u);
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        mode[k] = kNone;
+        if (q * 8 >= S) continue;
+        pl[k] = placeVector(sv, sv.tile[q / kTileVecs], q * 8, S);
+        if (!pl[k].inRun) {
+            mode[k] = kPerElement;
+        } else if (pgVec && (pl[k].addr0 & 7) == 0) {
+            mode[k] = kRegular;
+            x[k] = reinterpret_cast<const uint4 *>(G)[pl[k].addr0 >> 3];
+        } else {
+            mode[k] = kSemi;
+            x[k] = load8Narrow(G + pl[k].addr0);
+        }
     }
     double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < kNormVecPerLane; ++k) acc = sumSquares8(acc, x[k]);
+    for (int k = 0; k < kNormVecPerLane; ++k) {
+        if (mode[k] == kRegular || mode[k] == kSemi) {
+            acc = sumSquares8(acc, x[k]);
+        } else if (mode[k] == kPerElement) {
+            const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+            uint32_t run = pl[k].run;
+            for (int e = 0; e < 8; ++e) {
+                const uint64_t j = q * 8 + uint64_t(e);
+                if (j >= S) break;
+                uint64_t addr, rng;
+                placeElement(sv, run, j, addr, rng);
+                const double d = double(bf16At(G, addr));
+                acc = __builtin_fma(d, d, acc);
+            }
+        }
+    }
     const double total = blockSum<kBlock>(acc);
     if (threadIdx.x == 0) partials[tile] = total;
 }
@@ -365,28 +494,22 @@ __global__ __launch_bounds__(kBlock) void normReduceKernel(const double *__restr
     if (threadIdx.x == 0) out[blockIdx.x] = total;
 }
 
-__global__ __launch_bounds__(kNormFinishBlock) void normStage2Kernel(
-    const double *__restrict__ partials, uint64_t ntiles, const uint16_t *__restrict__ tail,
-    uint32_t ntail, float maxNorm, bfo_norm_result *__restrict__ out) {
+__global__ __launch_bounds__(kNormFinishBlock) void normStage2Kernel(const double *__restrict__ partials,
+                                                                     uint64_t count, float maxNorm,
+                                                                     bfo_norm_result *__restrict__ out) {
     // Lane t adds partials t, t+1024, t+2048, ... in that order; eight loads
     // are issued before their adds so the L2 round trips overlap.
     double acc = 0.0;
     uint64_t k = threadIdx.x;
     constexpr int kAhead = 8;
-    for (; k + (kAhead - 1) * kNormFinishBlock < ntiles; k += kAhead * kNormFinishBlock) {
+    for (; k + (kAhead - 1) * kNormFinishBlock < count; k += kAhead * kNormFinishBlock) {
         double p[kAhead];
 #pragma unroll
         for (int j = 0; j < kAhead; ++j) p[j] = partials[k + uint64_t(j) * kNormFinishBlock];
 #pragma unroll
         for (int j = 0; j < kAhead; ++j) acc += p[j];
     }
-    for (; k < ntiles; k += kNormFinishBlock) acc += partials[k];
-    if (threadIdx.x == 0) {
-        for (uint32_t e = 0; e < ntail; ++e) {
-            const double d = double(__uint_as_float(uint32_t(tail[e]) << 16));
-            acc = __builtin_fma(d, d, acc);
-        }
-    }
+    for (; k < count; k += kNormFinishBlock) acc += partials[k];
     const double sumsq = blockSum<kNormFinishBlock>(acc);
     if (threadIdx.x == 0) {
         const float norm = float(sqrt(sumsq));
@@ -409,13 +532,17 @@ __global__ __launch_bounds__(kBlock) void rngDumpKernel(uint64_t first, uint64_t
     out[k] = uint16_t(drawOf(d, int(i & 7)));
 }
 
-__global__ __launch_bounds__(kBlock) void decayDumpKernel(DecayView dv, uint64_t S, uint8_t *out,
+__global__ __launch_bounds__(kBlock) void decayDumpKernel(ShardView sv, uint64_t S, uint8_t *out,
                                                           uint64_t blockBase) {
     const uint64_t q = (blockBase + blockIdx.x) * kBlock + threadIdx.x;
     const uint64_t j0 = q * 8;
     if (j0 >= S) return;
-    const uint32_t mask = decayMask8(dv, dv.tile[j0 / kTileElems], j0);
-    for (int e = 0; e < 8 && j0 + e < S; ++e) out[j0 + e] = uint8_t((mask >> e) & 1u);
+    uint32_t run = sv.tile[q / kTileVecs] & ~kTileMixed;
+    for (int e = 0; e < 8 && j0 + e < S; ++e) {
+        uint64_t addr, rng;
+        placeElement(sv, run, j0 + e, addr, rng);
+        out[j0 + e] = sv.flag[run];
+    }
 }
 
 // A launch's lane count must stay below 2^32: split long 1-D grids.
@@ -423,37 +550,27 @@ constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 22;
 
 template <bool kMaster, int kRound>
 hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
-                        DecayView dv, StepScalars s, const float *scale, uint64_t group0,
-                        uint64_t seed, hipStream_t stream) {
+                        ShardView sv, int pgVec, StepScalars s, const float *scale, uint64_t seed,
+                        hipStream_t stream) {
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
-    const uint64_t nvec = S / 8;
-    const uint32_t ntail = uint32_t(S % 8);
-    if (nvec) {
-        const uint64_t tiles = (nvec + kTileVecs - 1) / kTileVecs;
-        for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
-            const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
-            hipLaunchKernelGGL((adamwTileKernel<kMaster, kRound>), dim3(uint32_t(nb)), dim3(kBlock), 0,
-                               stream, P, G, M, m, v, nvec, dv, s, scale, group0, k0, k1, base);
-        }
-    }
-    if (ntail) {
-        hipLaunchKernelGGL((adamwTailKernel<kMaster, kRound>), dim3(1), dim3(64), 0, stream, P, G, M, m,
-                           v, nvec * 8, ntail, dv, s, scale, group0 + nvec, k0, k1);
+    const uint64_t tiles = (S + kTileElems - 1) / kTileElems;
+    for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
+        const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL((adamwTileKernel<kMaster, kRound>), dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G,
+                           M, m, v, S, sv, pgVec, s, scale, k0, k1, base);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *partials,
-                      bfo_norm_result *out, hipStream_t stream) {
-    const uint64_t nvec = S / 8;
-    const uint32_t ntail = uint32_t(S % 8);
-    const uint64_t ntiles = normTiles(nvec);
+hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, float maxNorm,
+                      double *partials, bfo_norm_result *out, hipStream_t stream) {
+    const uint64_t ntiles = normTiles(S);
     for (uint64_t base = 0; base < ntiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = ntiles - base < kMaxBlocksPerLaunch ? ntiles - base : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, nvec, partials,
-                           base);
+        hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, S, sv, pgVec,
+                           partials, base);
     }
     const double *finishIn = partials;
     uint64_t finishCount = ntiles;
@@ -466,39 +583,31 @@ hipError_t launchNorm(const uint16_t *g, uint64_t S, float maxNorm, double *part
         finishCount = runs;
     }
     hipLaunchKernelGGL(normStage2Kernel, dim3(1), dim3(kNormFinishBlock), 0, stream, finishIn, finishCount,
-                       g + nvec * 8, ntail, maxNorm, out);
+                       maxNorm, out);
     return hipGetLastError();
 }
 
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
-                       DecayView dv, StepScalars s, const float *scale, uint64_t group0,
-                       uint64_t seed, int rounding, hipStream_t stream) {
+                       ShardView sv, int pgVec, StepScalars s, const float *scale, uint64_t seed,
+                       int rounding, hipStream_t stream) {
     if (M) {
         return rounding == BFO_ROUND_SR
-                   ? launchAdamwT<true, BFO_ROUND_SR>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream)
-                   : launchAdamwT<true, BFO_ROUND_RNE>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream);
+                   ? launchAdamwT<true, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream)
+                   : launchAdamwT<true, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream);
     }
     return rounding == BFO_ROUND_SR
-               ? launchAdamwT<false, BFO_ROUND_SR>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream)
-               : launchAdamwT<false, BFO_ROUND_RNE>(P, G, M, m, v, S, dv, s, scale, group0, seed, stream);
+               ? launchAdamwT<false, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream)
+               : launchAdamwT<false, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream);
 }
 
-hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, uint64_t group0,
+hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
                               uint64_t seed, hipStream_t stream) {
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
-    const uint64_t nvec = S / 8;
-    const uint32_t ntail = uint32_t(S % 8);
-    if (nvec) {
-        const uint64_t tiles = (nvec + kTileVecs - 1) / kTileVecs;
-        for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
-            const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
-            hipLaunchKernelGGL(masterToBf16Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P, nvec,
-                               group0, k0, k1, base);
-        }
-    }
-    if (ntail) {
-        hipLaunchKernelGGL(masterToBf16TailKernel, dim3(1), dim3(64), 0, stream, M, P, nvec * 8, ntail,
-                           group0 + nvec, k0, k1);
+    const uint64_t tiles = (S + kTileElems - 1) / kTileElems;
+    for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
+        const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL(masterToBf16Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P, S, sv, pgVec,
+                           k0, k1, base);
     }
     return hipGetLastError();
 }
@@ -516,13 +625,13 @@ hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t
     return hipGetLastError();
 }
 
-hipError_t launchDecayDump(DecayView dv, uint64_t S, uint8_t *out, hipStream_t stream) {
+hipError_t launchDecayDump(ShardView sv, uint64_t S, uint8_t *out, hipStream_t stream) {
     const uint64_t nv = (S + 7) / 8;
     if (nv) {
         const uint64_t blocks = (nv + kBlock - 1) / kBlock;
         for (uint64_t base = 0; base < blocks; base += kMaxBlocksPerLaunch) {
             const uint64_t nb = blocks - base < kMaxBlocksPerLaunch ? blocks - base : kMaxBlocksPerLaunch;
-            hipLaunchKernelGGL(decayDumpKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, dv, S, out, base);
+            hipLaunchKernelGGL(decayDumpKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, sv, S, out, base);
         }
     }
     return hipGetLastError();

@@ -21,15 +21,23 @@
  *   "LLM 分布式训练实战：CUDA/ROCm 多卡并行优化详解": §3.1 sharded update.
  *
  * Conventions shared by every entry point
- *   - Element layout.  A shard is the global element range [begin, end) of
- *     the flat buffer (see shard_range).  Every array argument is
- *     shard-local: element j of the array is global element begin + j, and
- *     the array holds end - begin elements.  bf16 values are passed as their
- *     16-bit patterns (uint16_t), fp32 values as float.
+ *   - Shards.  A table describes one rank's shard of the flat buffer, in one
+ *     of two layouts.  BFO_LAYOUT_FLAT: the contiguous global range
+ *     [begin, end) = [r*n/N, (r+1)*n/N) (see shard_range).  BFO_LAYOUT_PER_TENSOR:
+ *     rank r's 1/N slice of every tensor, concatenated in table order (the
+ *     llm.c rule that every tensor size divides by the process count).  The
+ *     shard holds S elements either way; shard-local element j maps to one
+ *     global index i of the flat buffer (bfo_table_runs lists the mapping).
+ *   - Arrays.  master, m and v are shard-local: element j of the array
+ *     belongs to shard element j; they hold S fp32 values.  params and grads
+ *     (bf16 patterns, uint16_t) are addressed differently per layout: FLAT --
+ *     shard-local too (element j; pass the full buffer + begin); PER_TENSOR --
+ *     the full n-element buffers (element i).
  *   - Memory.  Array arguments are device pointers on the device the table
- *     was created on, 16-byte aligned.  Scalars and the hyperparameter struct
- *     are host memory.  The caller owns every buffer; the library keeps no
- *     pointer after a call returns.
+ *     was created on.  master, m and v must be 16-byte aligned; params and
+ *     grads 2-byte aligned (16-byte aligned pointers take the fastest path).
+ *     Scalars and the hyperparameter struct are host memory.  The caller owns
+ *     every buffer; the library keeps no pointer after a call returns.
  *   - Asynchrony.  GPU work is queued on `stream` (a hipStream_t; NULL means
  *     the null stream) and the call returns without waiting for it.  Argument
  *     errors are reported synchronously and queue no work.  Nothing here
@@ -55,15 +63,17 @@ extern "C" {
 enum {
     BFO_OK = 0,
     BFO_EINVAL = -1,        /* null pointer, world == 0, t == 0, unknown rounding mode */
-    BFO_ENOTDIVISIBLE = -2, /* n is not a multiple of world */
+    BFO_ENOTDIVISIBLE = -2, /* n (or, per tensor, a tensor's size) is not a multiple of world */
     BFO_ERANGE = -3,        /* rank >= world */
-    BFO_EMISALIGNED = -4,   /* pointer not 16-byte aligned, or shard start not a multiple of 8 */
+    BFO_EMISALIGNED = -4,   /* pointer not aligned as required (see Memory above) */
     BFO_ETABLE = -5,        /* table not contiguous from 0, or undefined flag bits set */
     BFO_EHIP = -6,          /* a HIP runtime call failed */
     BFO_EDEVICE = -7        /* called with a different current device than the table's */
 };
 
 enum { BFO_ROUND_SR = 0, BFO_ROUND_RNE = 1 };
+
+enum { BFO_LAYOUT_FLAT = 0, BFO_LAYOUT_PER_TENSOR = 1 };
 
 /* bfo_tensor.flags bit 0: the tensor takes weight decay.  The pages apply
  * decay to 2-D tensors (embeddings, weight matrices) and not to 1-D ones
@@ -102,6 +112,21 @@ typedef struct {
  * the small device-side lookup it needs (created once, reused every step). */
 typedef struct bfo_table_s *bfo_table;
 
+/* One run of a shard plan: shard-local elements [local, local + length) are
+ * params/grads positions [addr, addr + length) and global indices
+ * [global, global + length) of the flat buffer, all in one tensor-flag
+ * class (flags bit 0 = decay).  addr equals local for FLAT tables and global
+ * for PER_TENSOR tables.  Consecutive pieces with the same flag that continue
+ * one another are merged into one run. */
+typedef struct {
+    uint64_t local;
+    uint64_t addr;
+    uint64_t global;
+    uint64_t length;
+    uint32_t flags;
+    uint32_t reserved;
+} bfo_run;
+
 /* ZeRO-1 shard of an n-element buffer over `world` ranks
  * ("04 · 多 GPU 与混合精度" §3.2: shard = parameter count / process count,
  * which must divide exactly; "LLM 分布式训练实战" §3.1: rank r starts at
@@ -111,26 +136,37 @@ typedef struct bfo_table_s *bfo_table;
 int shard_range(uint64_t n, uint32_t world, uint32_t rank, uint64_t *begin, uint64_t *end);
 
 /* Validates `tensors` (count entries, host memory, copied), takes rank
- * `rank`'s shard of the buffer they describe and uploads the per-shard
- * decay lookup to the current device.  The shard start must be a multiple
- * of 8 elements (it always is for world == 1; otherwise n / world must be a
- * multiple of 8): BFO_EMISALIGNED if not.  Other errors: as shard_range,
- * BFO_ETABLE, BFO_EINVAL (null out, or null tensors with count > 0),
- * BFO_EHIP.  The handle holds device memory until bfo_table_destroy. */
+ * `rank`'s BFO_LAYOUT_FLAT shard of the buffer they describe and uploads the
+ * shard plan to the current device.  Errors: as shard_range, BFO_ETABLE,
+ * BFO_EINVAL (null out, or null tensors with count > 0), BFO_EHIP.  The
+ * handle holds device memory until bfo_table_destroy. */
 int bfo_table_create(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
                      bfo_table *out);
+
+/* As bfo_table_create with an explicit layout (BFO_LAYOUT_FLAT or
+ * BFO_LAYOUT_PER_TENSOR).  PER_TENSOR ("04 · 多 GPU 与混合精度" §3.2 and §6:
+ * each tensor's size must divide by the process count) gives rank r
+ * elements [offset + r*numel/N, offset + (r+1)*numel/N) of every tensor;
+ * BFO_ENOTDIVISIBLE if any numel % world != 0.  Unknown layout: BFO_EINVAL. */
+int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
+                            int layout, bfo_table *out);
 
 /* Frees the handle and its device memory.  No call queued on the handle may
  * still be running.  NULL is accepted. */
 int bfo_table_destroy(bfo_table table);
 
-/* Buffer length n and the shard [begin, end) of a table. */
+/* Buffer length n and the shard of a table: FLAT -> [begin, end); PER_TENSOR
+ * -> begin = 0, end = S (the shard length). */
 int bfo_table_info(bfo_table table, uint64_t *n, uint64_t *begin, uint64_t *end);
+
+/* The table's shard plan: *count = number of runs; when out is not NULL,
+ * copies them (BFO_ERANGE if capacity < *count).  Host only. */
+int bfo_table_runs(bfo_table table, bfo_run *out, uint32_t capacity, uint32_t *count);
 
 /* Deterministic global grad norm of one shard ("04 · 多 GPU 与混合精度" §4:
  * grad_norm, then grad_scale = min(1, 1/grad_norm), i.e. clip to 1.0; under
  * ZeRO-1 this is the shard's part, which ranks would add before the root).
- * grads: end - begin bf16 patterns.  out: device bfo_norm_result.  Every
+ * grads: as in Arrays above.  out: device bfo_norm_result.  Every
  * square is formed and summed in binary64 over a fixed partition that
  * depends only on the shard length, so repeated calls give identical bits.
  * scale = max_norm / norm when norm > max_norm, else 1.0f (an infinite norm
@@ -157,6 +193,8 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo
  * et al., SC'11) with counter (lo32(i>>3), hi32(i>>3), 0, 0) and key
  * (lo32(seed), hi32(seed)); element i takes output word (i>>1)&3, low half
  * for even i.  RNE rounds to nearest, ties to even.  NaN stays NaN.
+ * i is element j's global index (its run's global + offset), so every
+ * layout and shard count draws the same r16 for the same parameter.
  * master == NULL selects the no-master path (old weights read from params).
  * scale: device float (e.g. &out->scale of grad_global_norm), or NULL for 1.
  * t: 1-based step number (0 -> BFO_EINVAL).  rounding: BFO_ROUND_SR/RNE. */
@@ -164,8 +202,8 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
                   float *v, const bfo_adamw_hparams *hp, const float *scale, uint64_t t,
                   uint64_t seed, int rounding, void *stream);
 
-/* Resume-time rebuild ("04 · 多 GPU 与混合精度" §5.2): params[j] =
- * SR(master[j], r16(begin + j, seed)) with the draws of adamw_sr_step, so
+/* Resume-time rebuild ("04 · 多 GPU 与混合精度" §5.2): params at element j's
+ * position = SR(master[j], r16(i, seed)) with the draws of adamw_sr_step, so
  * passing the seed of the update that produced `master` reproduces its
  * bf16 output bit for bit. */
 int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
@@ -176,7 +214,7 @@ int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, ui
 int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, void *stream);
 
 /* Test export: out[j] = 1 if shard element j's tensor has BFO_FLAG_DECAY,
- * else 0, as the update kernel sees it (device array of end - begin bytes). */
+ * else 0, as the update kernel sees it (device array of S bytes). */
 int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
 
 /* Static string naming a status code. */

@@ -67,6 +67,12 @@ def _load():
                                              _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_HParams),
                                              ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int]),
         "oracle_master_to_bf16_sr": (None, [_vp, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _vp]),
+        "oracle_adamw_step_mapped": (ctypes.c_int, [_vp, ctypes.c_uint32, _vp, ctypes.c_uint64,
+                                                    _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_HParams),
+                                                    ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int]),
+        "oracle_shard_map_per_tensor": (ctypes.c_int, [_vp, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                                       _vp, ctypes.c_uint64, _u64p]),
+        "oracle_master_to_bf16_sr_mapped": (None, [_vp, _vp, ctypes.c_uint64, ctypes.c_uint64, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -198,3 +204,39 @@ def master_to_bf16_sr(M, begin, seed):
     out = np.empty(M.size, np.uint16)
     _load().oracle_master_to_bf16_sr(_ptr(M), begin, M.size, seed, _ptr(out))
     return out
+
+
+def shard_map_per_tensor(tbl, world, rank):
+    """(status, global index of every shard position) for the per-tensor layout."""
+    total = int(tbl["numel"].sum()) if len(tbl) else 0
+    cap = total // world if world else 0
+    out = np.empty(max(cap, 1), np.uint64)
+    cnt = ctypes.c_uint64(0)
+    rc = _load().oracle_shard_map_per_tensor(_ptr(tbl), len(tbl), world, rank, _ptr(out), cap, ctypes.byref(cnt))
+    return rc, out[:cnt.value]
+
+
+def adamw_step_mapped(tbl, gidx, P_full, G_full, M, m, v, hp, grad_scale, t, seed, rounding=ROUND_SR):
+    """One step in place for shard positions j -> global gidx[j]; P_full, G_full
+    are full buffers, M/m/v shard-local."""
+    gidx = _need(np.ascontiguousarray(gidx, np.uint64), np.uint64, "gidx")
+    _need(P_full, np.uint16, "P_full")
+    _need(G_full, np.uint16, "G_full")
+    _need(m, np.float32, "m")
+    _need(v, np.float32, "v")
+    if M is not None:
+        _need(M, np.float32, "M")
+    n = gidx.size
+    if m.size != n or v.size != n or (M is not None and M.size != n):
+        raise ValueError("size mismatch")
+    rc = _load().oracle_adamw_step_mapped(_ptr(tbl), len(tbl), _ptr(gidx), n, _ptr(P_full), _ptr(G_full), _ptr(M),
+                                          _ptr(m), _ptr(v), ctypes.byref(hp), grad_scale, t, seed, rounding)
+    if rc != OK:
+        raise ValueError(f"oracle_adamw_step_mapped failed: {rc}")
+
+
+def master_to_bf16_sr_mapped(M, gidx, seed, P_full):
+    gidx = np.ascontiguousarray(gidx, np.uint64)
+    _need(M, np.float32, "M")
+    _need(P_full, np.uint16, "P_full")
+    _load().oracle_master_to_bf16_sr_mapped(_ptr(M), _ptr(gidx), gidx.size, seed, _ptr(P_full))

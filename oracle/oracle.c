@@ -281,9 +281,7 @@ static float lerp2fma(float start, float end, float w) {
     return fmaf(w, end, fmaf(-w, start, start));
 }
 
-/* One AdamW step over global elements [begin, begin + count) of the flat
- * buffer described by the table; element j of every array holds global
- * element begin + j.  Per element ([LLMC] §2.2, with [L13] §1.7 for the bias
+/* The AdamW step, per element ([LLMC] §2.2, with [L13] §1.7 for the bias
  * correction and the decoupled weight decay):
  *   grad = grad_scale * f32(G)
  *   m    = lerp(grad, m, beta1)           v = lerp(grad*grad, v, beta2)
@@ -293,50 +291,120 @@ static float lerp2fma(float start, float end, float w) {
  *   P    = SR(p, r16(i, seed))   or RNE(p)
  *   M    = p                     (master path only)
  * wd is the table's weight decay for 2-D tensors and 0 for the rest.
- * Each line below is one binary32 operation in this order. */
+ * adamw_element does one element (global index i, decay w); each of its
+ * lines is one binary32 operation, in the order above. */
+static void adamw_element(uint64_t i, float w, uint16_t *P, const uint16_t *G, float *M, float *m, float *v,
+                          const oracle_hparams *hp, float bc1, float bc2, float grad_scale,
+                          uint64_t seed, int rounding) {
+    float grad = grad_scale * oracle_bf16_to_f32(*G);
+    float m1 = lerp2fma(grad, *m, hp->beta1);
+    float gg = grad * grad;
+    float v1 = lerp2fma(gg, *v, hp->beta2);
+    float m_hat = m1 / bc1;
+    float v_hat = v1 / bc2;
+    float denom = sqrtf(v_hat) + hp->eps;
+    float adam = m_hat / denom;
+    float old = M ? *M : oracle_bf16_to_f32(*P);
+    float decay = w * old;
+    float sum = adam + decay;
+    float step = hp->lr * sum;
+    float p = old - step;
+
+    *m = m1;
+    *v = v1;
+    if (M) *M = p;
+    *P = (rounding == ORACLE_ROUND_SR) ? oracle_round_stochastic(p, oracle_rng16(i, seed))
+                                       : oracle_round_nearest_even(p);
+}
+
+static int step_args_check(const oracle_tensor *table, uint32_t ntensors, uint64_t *n, uint64_t t, int rounding) {
+    int rc = oracle_table_check(table, ntensors, n);
+    if (rc != ORACLE_OK) return rc;
+    if (t == 0) return ORACLE_EINVAL;
+    if (rounding != ORACLE_ROUND_SR && rounding != ORACLE_ROUND_RNE) return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* Index of the tensor holding global element i, searching forward from *k
+ * (and from 0 again when i lies before tensor *k). */
+static uint32_t tensor_of(const oracle_tensor *table, uint32_t ntensors, uint64_t i, uint32_t *k) {
+    if (*k >= ntensors || i < table[*k].offset) *k = 0;
+    while (*k < ntensors && i - table[*k].offset >= table[*k].numel) ++*k;
+    return *k;
+}
+
+/* One step over global elements [begin, begin + count); element j of every
+ * array holds global element begin + j. */
 int oracle_adamw_step(const oracle_tensor *table, uint32_t ntensors,
                       uint64_t begin, uint64_t count,
                       uint16_t *P, const uint16_t *G, float *M, float *m, float *v,
                       const oracle_hparams *hp, float grad_scale,
                       uint64_t t, uint64_t seed, int rounding) {
     uint64_t n;
-    int rc = oracle_table_check(table, ntensors, &n);
+    int rc = step_args_check(table, ntensors, &n, t, rounding);
     if (rc != ORACLE_OK) return rc;
     if (begin > n || count > n - begin) return ORACLE_ERANGE;
-    if (t == 0) return ORACLE_EINVAL;
-    if (rounding != ORACLE_ROUND_SR && rounding != ORACLE_ROUND_RNE) return ORACLE_EINVAL;
-
     float bc1, bc2;
     oracle_bias_corrections(hp->beta1, hp->beta2, t, hp->bias_correction, &bc1, &bc2);
-    const float beta1 = hp->beta1, beta2 = hp->beta2;
-    const float lr = hp->lr, eps = hp->eps;
-
     uint32_t k = 0;
     for (uint64_t j = 0; j < count; ++j) {
         uint64_t i = begin + j;
-        while (k < ntensors && i - table[k].offset >= table[k].numel) ++k;  /* tensor of element i */
+        tensor_of(table, ntensors, i, &k);
         float w = (table[k].flags & 1u) ? hp->weight_decay : 0.0f;
-
-        float grad = grad_scale * oracle_bf16_to_f32(G[j]);
-        float m1 = lerp2fma(grad, m[j], beta1);
-        float gg = grad * grad;
-        float v1 = lerp2fma(gg, v[j], beta2);
-        float m_hat = m1 / bc1;
-        float v_hat = v1 / bc2;
-        float denom = sqrtf(v_hat) + eps;
-        float adam = m_hat / denom;
-        float old = M ? M[j] : oracle_bf16_to_f32(P[j]);
-        float decay = w * old;
-        float sum = adam + decay;
-        float step = lr * sum;
-        float p = old - step;
-
-        m[j] = m1;
-        v[j] = v1;
-        if (M) M[j] = p;
-        P[j] = (rounding == ORACLE_ROUND_SR) ? oracle_round_stochastic(p, oracle_rng16(i, seed))
-                                             : oracle_round_nearest_even(p);
+        adamw_element(i, w, &P[j], &G[j], M ? &M[j] : NULL, &m[j], &v[j], hp, bc1, bc2, grad_scale, seed,
+                      rounding);
     }
+    return ORACLE_OK;
+}
+
+/* The same step for a shard given as a list of global indices: shard
+ * element j is global element gidx[j]; P and G are the full n-element
+ * buffers (indexed by global index), M, m and v are shard-local. */
+int oracle_adamw_step_mapped(const oracle_tensor *table, uint32_t ntensors,
+                             const uint64_t *gidx, uint64_t count,
+                             uint16_t *P, const uint16_t *G, float *M, float *m, float *v,
+                             const oracle_hparams *hp, float grad_scale,
+                             uint64_t t, uint64_t seed, int rounding) {
+    uint64_t n;
+    int rc = step_args_check(table, ntensors, &n, t, rounding);
+    if (rc != ORACLE_OK) return rc;
+    for (uint64_t j = 0; j < count; ++j)
+        if (gidx[j] >= n) return ORACLE_ERANGE;
+    float bc1, bc2;
+    oracle_bias_corrections(hp->beta1, hp->beta2, t, hp->bias_correction, &bc1, &bc2);
+    uint32_t k = 0;
+    for (uint64_t j = 0; j < count; ++j) {
+        uint64_t i = gidx[j];
+        tensor_of(table, ntensors, i, &k);
+        float w = (table[k].flags & 1u) ? hp->weight_decay : 0.0f;
+        adamw_element(i, w, &P[i], &G[i], M ? &M[j] : NULL, &m[j], &v[j], hp, bc1, bc2, grad_scale, seed,
+                      rounding);
+    }
+    return ORACLE_OK;
+}
+
+/* [LLMC] §3.2 and §6: llm.c shards every tensor, so each tensor's size must
+ * divide by the process count; rank r owns the r-th 1/N slice of each
+ * tensor, and its shard is those slices in table order.  Writes the global
+ * index of every shard position (count = n / world). */
+int oracle_shard_map_per_tensor(const oracle_tensor *table, uint32_t ntensors, uint32_t world, uint32_t rank,
+                                uint64_t *gidx, uint64_t capacity, uint64_t *count) {
+    uint64_t n;
+    int rc = oracle_table_check(table, ntensors, &n);
+    if (rc != ORACLE_OK) return rc;
+    if (world == 0) return ORACLE_EINVAL;
+    if (rank >= world) return ORACLE_ERANGE;
+    for (uint32_t k = 0; k < ntensors; ++k)
+        if (table[k].numel % world != 0) return ORACLE_ENOTDIVISIBLE;
+    uint64_t j = 0;
+    for (uint32_t k = 0; k < ntensors; ++k) {
+        uint64_t slice = table[k].numel / world;
+        for (uint64_t e = 0; e < slice; ++e) {
+            if (j >= capacity) return ORACLE_ERANGE;
+            gidx[j++] = table[k].offset + (uint64_t)rank * slice + e;
+        }
+    }
+    *count = j;
     return ORACLE_OK;
 }
 
@@ -347,6 +415,13 @@ int oracle_adamw_step(const oracle_tensor *table, uint32_t ntensors,
 void oracle_master_to_bf16_sr(const float *M, uint64_t begin, uint64_t count, uint64_t seed, uint16_t *P) {
     for (uint64_t j = 0; j < count; ++j)
         P[j] = oracle_round_stochastic(M[j], oracle_rng16(begin + j, seed));
+}
+
+/* The same for a shard given by global indices: P_full[gidx[j]] = SR(M[j]). */
+void oracle_master_to_bf16_sr_mapped(const float *M, const uint64_t *gidx, uint64_t count, uint64_t seed,
+                                     uint16_t *P_full) {
+    for (uint64_t j = 0; j < count; ++j)
+        P_full[gidx[j]] = oracle_round_stochastic(M[j], oracle_rng16(gidx[j], seed));
 }
 
 /* Array helper for the test harness: widen bf16 patterns to binary32. */

@@ -75,8 +75,13 @@ def test_table_create_rejects_bad_tables_before_touching_the_gpu(bfo):
     assert _create(bfo, [(0, 2**64 - 1, 0), (2**64 - 1, 5, 0)])[0] == bfo.ETABLE  # overflow
     assert _create(bfo, [(0, 30, 1)], world=4)[0] == bfo.ENOTDIVISIBLE
     assert _create(bfo, [(0, 32, 1)], world=4, rank=4)[0] == bfo.ERANGE
-    assert _create(bfo, [(0, 36, 1)], world=4, rank=1)[0] == bfo.EMISALIGNED  # shard start 9
     assert _create(bfo, [(0, 32, 1)], world=0)[0] == bfo.EINVAL
+    lib = bfo.library()
+    arr = (bfo.BfoTensor * 2)()
+    arr[0].offset, arr[0].numel, arr[1].offset, arr[1].numel = 0, 8, 8, 6   # 6 % 4 != 0
+    h = ctypes.c_void_p(None)
+    assert lib.bfo_table_create_layout(arr, 2, 4, 0, bfo.LAYOUT_PER_TENSOR, ctypes.byref(h)) == bfo.ENOTDIVISIBLE
+    assert lib.bfo_table_create_layout(arr, 2, 2, 0, 7, ctypes.byref(h)) == bfo.EINVAL   # unknown layout
     lib = bfo.library()
     assert lib.bfo_table_create(None, 3, 1, 0, ctypes.byref(ctypes.c_void_p())) == bfo.EINVAL
     arr = (bfo.BfoTensor * 1)()
@@ -91,6 +96,7 @@ def test_entry_points_reject_null_table_and_bad_scalars(bfo):
     assert lib.master_to_bf16_sr(None, None, None, 0, None) == bfo.EINVAL
     assert lib.bfo_decay_mask_dump(None, None, None) == bfo.EINVAL
     assert lib.bfo_table_info(None, None, None, None) == bfo.EINVAL
+    assert lib.bfo_table_runs(None, None, 0, ctypes.byref(ctypes.c_uint32())) == bfo.EINVAL
     assert lib.bfo_table_destroy(None) == bfo.OK
     assert lib.bfo_rng_dump(0, 10, 0, None, None) == bfo.EINVAL
     assert lib.bfo_rng_dump(0, 10, 0, ctypes.c_void_p(1), None) == bfo.EMISALIGNED

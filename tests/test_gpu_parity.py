@@ -441,3 +441,143 @@ def test_full_size_llama7b(bfo):
     got = full_size_step(bfo, w, 0, steps=1)
     print(f"llama7b: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
     assert got[2] < 1.0
+
+
+# --------------------------------------------------------------------- layouts
+
+
+def padded_tiny(pad):
+    """The d=32 model plus a trailing 1-D tensor of `pad` elements, so that
+    n / world stops being a multiple of 8 (misaligned flat shard starts)."""
+    w = W.tiny()
+    w.tensors = list(w.tensors) + [("pad", (pad,))]
+    return w
+
+
+LAYOUT_CASES = [("flat", W.tiny, 8), ("flat_misaligned", lambda: padded_tiny(4), 4),
+                ("per_tensor", W.tiny, 8), ("per_tensor", W.tiny, 2)]
+
+
+def _oracle_gidx(bfo, tbl, w, world, rank, layout):
+    if layout == bfo.LAYOUT_PER_TENSOR:
+        rc, g = o.shard_map_per_tensor(tbl, world, rank)
+        assert rc == o.OK
+        return g
+    rc, b, e = o.shard_range(w.n, world, rank)
+    assert rc == o.OK
+    return np.arange(b, e, dtype=np.uint64)
+
+
+@pytest.mark.parametrize("name,make,world", LAYOUT_CASES)
+def test_shard_plan_matches_oracle(bfo, name, make, world):
+    w = make()
+    ents = w.entries()
+    tbl = o.table(ents)
+    layout = bfo.LAYOUT_PER_TENSOR if name == "per_tensor" else bfo.LAYOUT_FLAT
+    decay_all = o.decay_mask(tbl, 0, w.n)
+    for r in range(world):
+        T = bfo.Table(ents, world, r, layout=layout)
+        gidx = _oracle_gidx(bfo, tbl, w, world, r, layout)
+        assert np.array_equal(T.global_index(), gidx), (name, r)
+        dm = bfo.decay_mask_dump(T).cpu().numpy()
+        assert np.array_equal(dm, decay_all[gidx]), (name, r)
+
+
+@pytest.mark.parametrize("name,make,world", LAYOUT_CASES)
+@pytest.mark.parametrize("master", [True, False])
+def test_update_layouts_all_ranks(bfo, name, make, world, master):
+    # Every rank's shard is stepped on the GPU and by the oracle from the same
+    # full initial state; the shards together must also rebuild the unsharded
+    # GPU run bit for bit.  The clip scale is the global one (world=1 norm).
+    w = make()
+    w.grad_std = 0.05                                    # clip active
+    ents = w.entries()
+    tbl = o.table(ents)
+    layout = bfo.LAYOUT_PER_TENSOR if name == "per_tensor" else bfo.LAYOUT_FLAT
+    P0, M0, _, _ = W.init_state(torch, w, 0, w.n, DEV)
+    Gs = []
+    for t in range(1, 4):
+        G = torch.empty(w.n, dtype=torch.bfloat16, device=DEV)
+        W.fill_grads(torch, w, G, 0, t)
+        Gs.append(G)
+    Tfull = bfo.Table(ents)
+    res = bfo.new_norm_result(DEV)
+
+    # unsharded reference run on the GPU
+    ref = {"P": P0.clone(), "M": M0.clone(), "m": torch.zeros(w.n, device=DEV), "v": torch.zeros(w.n, device=DEV)}
+    for t, G in enumerate(Gs, 1):
+        bfo.grad_global_norm(Tfull, G, res)
+        bfo.adamw_sr_step(Tfull, ref["P"], G, ref["M"] if master else None, ref["m"], ref["v"], w.hparams, t,
+                          step_seed(t), scale=res)
+
+    P = P0.clone()
+    Ph = u16(P0)
+    Gh = [u16(G) for G in Gs]
+    ranks = []
+    for r in range(world):
+        T = bfo.Table(ents, world, r, layout=layout)
+        gidx = _oracle_gidx(bfo, tbl, w, world, r, layout)
+        gi = torch.from_numpy(gidx.astype(np.int64)).to(DEV)
+        st = {"M": M0[gi].clone() if master else None, "m": torch.zeros(T.size, device=DEV),
+              "v": torch.zeros(T.size, device=DEV)}
+        h = {"M": f32(st["M"]) if master else None, "m": np.zeros(T.size, np.float32),
+             "v": np.zeros(T.size, np.float32)}
+        ranks.append((T, gidx, st, h))
+    for t, G in enumerate(Gs, 1):
+        bfo.grad_global_norm(Tfull, G, res)
+        scale = bfo.read_norm_result(res)[2]
+        for T, gidx, st, h in ranks:
+            if layout == bfo.LAYOUT_PER_TENSOR:
+                Pa, Ga = P, G
+            else:
+                Pa, Ga = P[T.begin:T.end], G[T.begin:T.end]
+            rres = bfo.new_norm_result(DEV)
+            bfo.grad_global_norm(T, Ga, rres)
+            assert_norm_parity(bfo.read_norm_result(rres), o.grad_norm(np.ascontiguousarray(Gh[t - 1][gidx])))
+            bfo.adamw_sr_step(T, Pa, Ga, st["M"], st["m"], st["v"], w.hparams, t, step_seed(t), scale=res)
+            o.adamw_step_mapped(tbl, gidx, Ph, Gh[t - 1], h["M"], h["m"], h["v"], oracle_hparams(w.hparams), scale,
+                                t, step_seed(t))
+    assert_bf16_parity(u16(P), Ph, f"{name} params")
+    assert np.array_equal(u16(P), u16(ref["P"])), "sharded run differs from the unsharded one"
+    for T, gidx, st, h in ranks:
+        gi = torch.from_numpy(gidx.astype(np.int64)).to(DEV)
+        for k in ("m", "v") + (("M",) if master else ()):
+            assert_f32_parity(f32(st[k]), h[k], f"{name} {k}")
+            assert np.array_equal(f32(st[k]).view(np.uint32), f32(ref[k][gi]).view(np.uint32)), (name, k)
+    if master:
+        # replay: every rank rebuilds its own bf16 params from its master
+        Pr = torch.zeros_like(P)
+        for T, gidx, st, h in ranks:
+            Pa = Pr if layout == bfo.LAYOUT_PER_TENSOR else Pr[T.begin:T.end]
+            bfo.master_to_bf16_sr(T, st["M"], Pa, step_seed(3))
+        assert np.array_equal(u16(Pr), u16(P))
+
+
+def test_update_per_tensor_gpt2_124m(bfo):
+    w = W.gpt2_124m()
+    ents = w.entries()
+    tbl = o.table(ents)
+    world, r = 4, 1
+    T = bfo.Table(ents, world, r, layout=bfo.LAYOUT_PER_TENSOR)
+    gidx = _oracle_gidx(bfo, tbl, w, world, r, bfo.LAYOUT_PER_TENSOR)
+    assert np.array_equal(T.global_index(), gidx)
+    P, M0, _, _ = W.init_state(torch, w, 0, w.n, DEV)
+    gi = torch.from_numpy(gidx.astype(np.int64)).to(DEV)
+    st = {"M": M0[gi].clone(), "m": torch.zeros(T.size, device=DEV), "v": torch.zeros(T.size, device=DEV)}
+    del M0
+    h = {"M": f32(st["M"]), "m": np.zeros(T.size, np.float32), "v": np.zeros(T.size, np.float32)}
+    Ph = u16(P)
+    G = torch.empty(w.n, dtype=torch.bfloat16, device=DEV)
+    res = bfo.new_norm_result(DEV)
+    for t in (1, 2):
+        W.fill_grads(torch, w, G, 0, t)
+        Gh = u16(G)
+        bfo.grad_global_norm(T, G, res)
+        got = bfo.read_norm_result(res)
+        assert_norm_parity(got, o.grad_norm(np.ascontiguousarray(Gh[gidx])))
+        bfo.adamw_sr_step(T, P, G, st["M"], st["m"], st["v"], w.hparams, t, step_seed(t), scale=res)
+        o.adamw_step_mapped(tbl, gidx, Ph, Gh, h["M"], h["m"], h["v"], oracle_hparams(w.hparams), got[2], t,
+                            step_seed(t))
+        assert_bf16_parity(u16(P), Ph, "per-tensor 124M params")
+        for k in ("M", "m", "v"):
+            assert_f32_parity(f32(st[k]), h[k], f"per-tensor 124M {k}")

@@ -422,3 +422,60 @@ def test_stall_sr_tracks_master_rne_freezes():
     diff = bf16_value(B[0]) - A[1].astype(np.float64)
     assert abs(drift_sr.mean() - drift_master.mean()) <= 3 * diff.std() / math.sqrt(n)
     assert np.array_equal(C[0], P0)                                # frozen
+
+
+def test_per_tensor_shard_map_partitions_the_buffer():
+    # "04 · 多 GPU 与混合精度" §3.2 and §6: with llm.c's per-tensor sharding
+    # every tensor size must divide by the process count; the N ranks' maps
+    # together cover every element exactly once, n/N each.
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    for world in (1, 2, 4, 8):
+        seen = []
+        for r in range(world):
+            rc, gidx = o.shard_map_per_tensor(tbl, world, r)
+            assert rc == o.OK and gidx.size == w.n // world
+            assert np.all(np.diff(gidx.astype(np.int64)) > 0)            # increasing global order
+            seen.append(gidx)
+        allidx = np.sort(np.concatenate(seen))
+        assert np.array_equal(allidx, np.arange(w.n, dtype=np.uint64))
+    assert o.shard_map_per_tensor(tbl, 3, 0)[0] == o.ENOTDIVISIBLE        # 32-element tensors over 3
+    assert o.shard_map_per_tensor(tbl, 4, 4)[0] == o.ERANGE
+    # every rank owns 1/N of every tensor
+    rc, g = o.shard_map_per_tensor(tbl, 4, 2)
+    for off, numel, _ in w.entries():
+        inside = (g >= off) & (g < off + numel)
+        assert inside.sum() == numel // 4
+
+
+def test_per_tensor_sharded_steps_equal_unsharded():
+    # Any partition of the elements gives the unsharded result bit for bit:
+    # the update is elementwise and every draw is keyed on the global index.
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    rs = np.random.default_rng(44)
+    P0 = to_bf16_bits_torch((rs.standard_normal(w.n) * 0.02).astype(np.float32))
+    Gs = [to_bf16_bits_torch((rs.standard_normal(w.n) * 1e-3).astype(np.float32)) for _ in range(3)]
+    hp = o.hparams(**HP)
+    P = P0.copy()
+    M, m, v = _bits_f32(P0), np.zeros(w.n, np.float32), np.zeros(w.n, np.float32)
+    for t, G in enumerate(Gs, 1):
+        o.adamw_step(tbl, 0, P, G, M, m, v, hp, 1.0, t, (1337 << 32) | t, o.ROUND_SR)
+    for world in (2, 8):
+        Pw = P0.copy()
+        parts = []
+        for r in range(world):
+            _, gidx = o.shard_map_per_tensor(tbl, world, r)
+            Mr, mr, vr = _bits_f32(P0[gidx]), np.zeros(gidx.size, np.float32), np.zeros(gidx.size, np.float32)
+            for t, G in enumerate(Gs, 1):
+                o.adamw_step_mapped(tbl, gidx, Pw, G, Mr, mr, vr, hp, 1.0, t, (1337 << 32) | t, o.ROUND_SR)
+            parts.append((gidx, Mr, mr, vr))
+        assert np.array_equal(Pw, P)
+        for gidx, Mr, mr, vr in parts:
+            assert np.array_equal(Mr.view(np.uint32), M[gidx].view(np.uint32))
+            assert np.array_equal(mr.view(np.uint32), m[gidx].view(np.uint32))
+            assert np.array_equal(vr.view(np.uint32), v[gidx].view(np.uint32))
+        Pr = np.zeros(w.n, np.uint16)
+        for gidx, Mr, _, _ in parts:
+            o.master_to_bf16_sr_mapped(Mr, gidx, (1337 << 32) | 3, Pr)
+        assert np.array_equal(Pr, P)
