@@ -31,7 +31,10 @@ LAYOUT_PER_TENSOR = 1
 EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_table_destroy",
            "bfo_table_info", "bfo_table_runs",
            "grad_global_norm", "adamw_sr_step", "master_to_bf16_sr", "bfo_rng_dump",
-           "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error")
+           "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error", "bfo_lr_at",
+           "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update")
+
+LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
 
 class BfoTensor(ctypes.Structure):
@@ -48,6 +51,12 @@ class AdamwHParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("bias_correction", ctypes.c_int32)]
+
+
+class LrSchedule(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_uint32), ("warmup_steps", ctypes.c_uint64),
+                ("total_steps", ctypes.c_uint64), ("lr_max", ctypes.c_float), ("final_frac", ctypes.c_float),
+                ("decay_frac", ctypes.c_float), ("reserved2", ctypes.c_uint32)]
 
 
 NORM_RESULT_BYTES = 16  # bfo_norm_result: double sumsq; float norm; float scale
@@ -83,7 +92,12 @@ def _lib():
         "bfo_table_destroy": (i32, [vp]),
         "bfo_table_info": (i32, [vp, pu64, pu64, pu64]),
         "grad_global_norm": (i32, [vp, vp, ctypes.c_float, vp, vp]),
-        "adamw_sr_step": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, u64, u64, i32, vp]),
+        "adamw_sr_step": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, vp, u64, u64, i32, vp]),
+        "bfo_lr_at": (i32, [ctypes.POINTER(LrSchedule), u64, ctypes.POINTER(ctypes.c_float)]),
+        "bfo_outlier_create": (i32, [u32, ctypes.c_float, ctypes.POINTER(vp)]),
+        "bfo_outlier_destroy": (i32, [vp]),
+        "bfo_outlier_reset": (i32, [vp, vp]),
+        "bfo_outlier_update": (i32, [vp, vp, vp, vp, vp]),
         "master_to_bf16_sr": (i32, [vp, vp, vp, u64, vp]),
         "bfo_rng_dump": (i32, [u64, u64, u64, vp, vp]),
         "bfo_decay_mask_dump": (i32, [vp, vp, vp]),
@@ -245,9 +259,11 @@ def grad_global_norm(table, grads, out, max_norm=1.0):
 
 
 def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
-                  rounding=ROUND_SR):
+                  rounding=ROUND_SR, skip=None):
     """One fused AdamW step over the shard.  scale: a norm-result buffer
-    (its .scale is used), an int device address, or None for 1.0."""
+    (its .scale is used), an int device address, or None for 1.0.  skip: an
+    int32 device tensor of one element (nonzero -> the step changes nothing)
+    or None."""
     dev = table.device
     S = table.size
     p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
@@ -263,11 +279,65 @@ def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
         sp = None
     else:
         sp = ctypes.c_void_p(int(scale))
+    sk = _arg(skip, torch.int32, 1, "skip", dev) if skip is not None else None
     h = hp if isinstance(hp, AdamwHParams) else AdamwHParams(
         hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1 if hp.bias_correction else 0)
     with torch.cuda.device(dev):
-        _check("adamw_sr_step", _lib().adamw_sr_step(table.handle, p, g, M, mm, vv, ctypes.byref(h), sp,
+        _check("adamw_sr_step", _lib().adamw_sr_step(table.handle, p, g, M, mm, vv, ctypes.byref(h), sp, sk,
                                                      t, seed, rounding, _stream(dev)))
+
+
+def lr_at(kind, step, warmup_steps, total_steps, lr_max, final_frac=0.0, decay_frac=0.0):
+    """The library's learning-rate schedule at 0-based `step` (host only)."""
+    sch = LrSchedule(kind, 0, warmup_steps, total_steps, lr_max, final_frac, decay_frac, 0)
+    out = ctypes.c_float(0.0)
+    _check("bfo_lr_at", _lib().bfo_lr_at(ctypes.byref(sch), step, ctypes.byref(out)))
+    return out.value
+
+
+class Outlier:
+    """Device-side z-score detector over the last `window` values."""
+
+    def __init__(self, window=128, threshold=0.0, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else
+                                   torch.device(device).index or 0)
+        h = ctypes.c_void_p(None)
+        with torch.cuda.device(self.device):
+            _check("bfo_outlier_create", _lib().bfo_outlier_create(window, threshold, ctypes.byref(h)))
+        self._h = h
+        self.z = torch.zeros(1, dtype=torch.float32, device=self.device)
+        self.skip = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    def update(self, value_ptr):
+        """Queue an update reading the device float at `value_ptr` (an int
+        address or a one-element float32 tensor); fills self.z, self.skip."""
+        vp = value_ptr.data_ptr() if isinstance(value_ptr, torch.Tensor) else int(value_ptr)
+        with torch.cuda.device(self.device):
+            _check("bfo_outlier_update", _lib().bfo_outlier_update(
+                self._h, ctypes.c_void_p(vp), ctypes.c_void_p(self.z.data_ptr()),
+                ctypes.c_void_p(self.skip.data_ptr()), _stream(self.device)))
+        return self
+
+    def reset(self):
+        with torch.cuda.device(self.device):
+            _check("bfo_outlier_reset", _lib().bfo_outlier_reset(self._h, _stream(self.device)))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            torch.cuda.synchronize(self.device)
+            _check("bfo_outlier_destroy", _lib().bfo_outlier_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def norm_ptr(res):
+    """Address of bfo_norm_result.norm inside a norm-result buffer."""
+    return res.data_ptr() + 8
 
 
 def master_to_bf16_sr(table, master, params, seed):

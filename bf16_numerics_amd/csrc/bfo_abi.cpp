@@ -16,14 +16,16 @@ namespace {
 
 thread_local int gLastHipError = 0;
 
-int hipFail(hipError_t e) {
-    gLastHipError = int(e);
-    return BFO_EHIP;
-}
+int hipFail(hipError_t e) { return bfo::recordHipFailure(e); }
 
 bool alignedTo(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
+
+int bfo::recordHipFailure(hipError_t e) {
+    gLastHipError = int(e);
+    return BFO_EHIP;
+}
 
 struct bfo_table_s {
     uint64_t n = 0, S = 0, begin = 0;
@@ -243,14 +245,14 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo
 }
 
 int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
-                  float *v, const bfo_adamw_hparams *hp, const float *scale, uint64_t t,
+                  float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
                   uint64_t seed, int rounding, void *stream) {
     if (!table || !hp || t == 0) return BFO_EINVAL;
     if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
     const uint64_t S = table->S;
     if (S && (!params || !grads || !m || !v)) return BFO_EINVAL;
     if (!alignedTo(params, 2) || !alignedTo(grads, 2) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
-        !alignedTo(v, 16) || !alignedTo(scale, 4))
+        !alignedTo(v, 16) || !alignedTo(scale, 4) || !alignedTo(skip, 4))
         return BFO_EMISALIGNED;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
@@ -268,8 +270,8 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
     s.bc2 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta2), double(t))) : 1.0f;
 
     const int pgVec = alignedTo(params, 16) && alignedTo(grads, 16) ? 1 : 0;
-    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, scale, seed,
-                                     rounding, static_cast<hipStream_t>(stream));
+    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, scale, skip,
+                                     seed, rounding, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 

@@ -55,6 +55,9 @@ struct StepScalars {
     float lr, beta1, beta2, eps, wd, bc1, bc2;
 };
 
+// Records a failed HIP call for bfo_last_hip_error() and returns BFO_EHIP.
+int recordHipFailure(hipError_t e);
+
 // Launchers (bfo_kernels.hip).  Shapes are checked by the caller: M, m, v
 // hold S shard-local elements, 16-byte aligned; P and G are addressed
 // through the runs and are at least 2-byte aligned; pgVec says whether P
@@ -63,12 +66,24 @@ struct StepScalars {
 hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, float maxNorm,
                       double *partials, bfo_norm_result *out, hipStream_t stream);
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
-                       ShardView sv, int pgVec, StepScalars s, const float *scale, uint64_t seed,
-                       int rounding, hipStream_t stream);
+                       ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
+                       uint64_t seed, int rounding, hipStream_t stream);
 hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
                               uint64_t seed, hipStream_t stream);
 hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out,
                          hipStream_t stream);
 hipError_t launchDecayDump(ShardView sv, uint64_t S, uint8_t *out, hipStream_t stream);
+
+// Outlier detector state in device memory: a ring of the last `window`
+// finite values (oldest at `head` once full).
+struct OutlierState {
+    uint32_t window, count, head, pad;
+    float values[1];  // [window]
+};
+constexpr uint32_t kOutlierMaxWindow = 4096;
+
+hipError_t launchOutlierUpdate(OutlierState *state, const float *value, float threshold, float *z,
+                               int32_t *skip, hipStream_t stream);
+hipError_t launchOutlierReset(OutlierState *state, uint32_t window, hipStream_t stream);
 
 }  // namespace bfo

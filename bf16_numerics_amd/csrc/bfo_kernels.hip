@@ -226,7 +226,9 @@ template <bool kMaster, int kRound>
 __global__ __launch_bounds__(kBlock) void adamwTileKernel(
     uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
     float *__restrict__ Mom, float *__restrict__ Var, uint64_t S, ShardView sv, int pgVec, StepScalars s,
-    const float *__restrict__ scalePtr, uint32_t key0, uint32_t key1, uint64_t tileBase) {
+    const float *__restrict__ scalePtr, const int32_t *__restrict__ skipPtr, uint32_t key0, uint32_t key1,
+    uint64_t tileBase) {
+    if (skipPtr && *skipPtr) return;  // step control decided to skip this update
     const float scale = scalePtr ? *scalePtr : 1.0f;
     const uint64_t tile = tileBase + blockIdx.x;
     const uint32_t tileWord = sv.tile[tile];
@@ -548,16 +550,63 @@ __global__ __launch_bounds__(kBlock) void decayDumpKernel(ShardView sv, uint64_t
 // A launch's lane count must stay below 2^32: split long 1-D grids.
 constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 22;
 
+// ---------------------------------------------------------------------------
+// Outlier z-score ("04 · 多 GPU 与混合精度" §4): one lane compares the new
+// value with the window of previous finite values (binary64 mean and
+// population variance, summed oldest to newest), writes z (NaN until the
+// window is full) and the skip flag, then appends the value if finite.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void outlierUpdateKernel(OutlierState *st, const float *value, float threshold,
+                                                          float *zOut, int32_t *skipOut) {
+    if (threadIdx.x != 0) return;
+    const float x = *value;
+    const uint32_t W = st->window;
+    double z = __builtin_nan("");
+    if (st->count == W) {
+        double sum = 0.0;
+        for (uint32_t k = 0; k < W; ++k) {
+            uint32_t idx = st->head + k;
+            if (idx >= W) idx -= W;
+            sum += double(st->values[idx]);
+        }
+        const double mean = sum / double(W);
+        double sq = 0.0;
+        for (uint32_t k = 0; k < W; ++k) {
+            uint32_t idx = st->head + k;
+            if (idx >= W) idx -= W;
+            const double dev = double(st->values[idx]) - mean;
+            sq += dev * dev;
+        }
+        z = (double(x) - mean) / sqrt(sq / double(W));
+    }
+    const bool finite = (__float_as_uint(x) & 0x7F800000u) != 0x7F800000u;
+    *zOut = float(z);
+    *skipOut = (!finite || (threshold > 0.0f && z > double(threshold))) ? 1 : 0;
+    if (finite) {
+        st->values[st->head] = x;
+        st->head = st->head + 1 == W ? 0u : st->head + 1;
+        if (st->count < W) st->count = st->count + 1;
+    }
+}
+
+__global__ __launch_bounds__(64) void outlierResetKernel(OutlierState *st, uint32_t window) {
+    if (threadIdx.x != 0) return;
+    st->window = window;
+    st->count = 0;
+    st->head = 0;
+    st->pad = 0;
+}
+
 template <bool kMaster, int kRound>
 hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
-                        ShardView sv, int pgVec, StepScalars s, const float *scale, uint64_t seed,
-                        hipStream_t stream) {
+                        ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
+                        uint64_t seed, hipStream_t stream) {
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
     const uint64_t tiles = (S + kTileElems - 1) / kTileElems;
     for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
         hipLaunchKernelGGL((adamwTileKernel<kMaster, kRound>), dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G,
-                           M, m, v, S, sv, pgVec, s, scale, k0, k1, base);
+                           M, m, v, S, sv, pgVec, s, scale, skip, k0, k1, base);
     }
     return hipGetLastError();
 }
@@ -588,16 +637,27 @@ hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, fl
 }
 
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
-                       ShardView sv, int pgVec, StepScalars s, const float *scale, uint64_t seed,
-                       int rounding, hipStream_t stream) {
+                       ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
+                       uint64_t seed, int rounding, hipStream_t stream) {
     if (M) {
         return rounding == BFO_ROUND_SR
-                   ? launchAdamwT<true, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream)
-                   : launchAdamwT<true, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream);
+                   ? launchAdamwT<true, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream)
+                   : launchAdamwT<true, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream);
     }
     return rounding == BFO_ROUND_SR
-               ? launchAdamwT<false, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream)
-               : launchAdamwT<false, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, seed, stream);
+               ? launchAdamwT<false, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream)
+               : launchAdamwT<false, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream);
+}
+
+hipError_t launchOutlierUpdate(OutlierState *state, const float *value, float threshold, float *z,
+                               int32_t *skip, hipStream_t stream) {
+    hipLaunchKernelGGL(outlierUpdateKernel, dim3(1), dim3(64), 0, stream, state, value, threshold, z, skip);
+    return hipGetLastError();
+}
+
+hipError_t launchOutlierReset(OutlierState *state, uint32_t window, hipStream_t stream) {
+    hipLaunchKernelGGL(outlierResetKernel, dim3(1), dim3(64), 0, stream, state, window);
+    return hipGetLastError();
 }
 
 hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,

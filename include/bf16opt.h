@@ -197,9 +197,12 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo
  * layout and shard count draws the same r16 for the same parameter.
  * master == NULL selects the no-master path (old weights read from params).
  * scale: device float (e.g. &out->scale of grad_global_norm), or NULL for 1.
+ * skip: device int32 (e.g. written by bfo_outlier_update), or NULL; when it
+ * holds a nonzero value at run time the step changes nothing (every
+ * workgroup exits after reading it).
  * t: 1-based step number (0 -> BFO_EINVAL).  rounding: BFO_ROUND_SR/RNE. */
 int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
-                  float *v, const bfo_adamw_hparams *hp, const float *scale, uint64_t t,
+                  float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
                   uint64_t seed, int rounding, void *stream);
 
 /* Resume-time rebuild ("04 · 多 GPU 与混合精度" §5.2): params at element j's
@@ -216,6 +219,50 @@ int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, v
 /* Test export: out[j] = 1 if shard element j's tensor has BFO_FLAG_DECAY,
  * else 0, as the update kernel sees it (device array of S bytes). */
 int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
+
+/* Learning-rate schedules ("04 · 多 GPU 与混合精度" §4 names cosine, linear,
+ * constant and wsd; the formulas are this library's reading).  For 0-based
+ * step s, lr_min = final_frac * lr_max, W = warmup_steps, T = total_steps:
+ *   s < W: lr_max * (s + 1) / W (every kind);
+ *   then, with p = min(1, (s - W) / (T - W)) (p = 1 when T == W):
+ *   CONSTANT lr_max; LINEAR lr_max - (lr_max - lr_min) * p;
+ *   COSINE lr_min + (lr_max - lr_min) * (1 + cos(pi * p)) / 2;
+ *   WSD lr_max until s >= T - D with D = decay_frac * T, then linear from
+ *   lr_max to lr_min over those last D steps.
+ * Evaluated in binary64, rounded once to binary32.  Host only. */
+enum { BFO_LR_CONSTANT = 0, BFO_LR_LINEAR = 1, BFO_LR_COSINE = 2, BFO_LR_WSD = 3 };
+typedef struct {
+    int32_t kind;
+    uint32_t reserved;
+    uint64_t warmup_steps;
+    uint64_t total_steps;   /* >= warmup_steps */
+    float lr_max;
+    float final_frac;
+    float decay_frac;       /* WSD only */
+    uint32_t reserved2;
+} bfo_lr_schedule;
+
+/* *lr = the schedule's learning rate at step `step`.  BFO_EINVAL for a null
+ * argument, an unknown kind or total_steps < warmup_steps. */
+int bfo_lr_at(const bfo_lr_schedule *schedule, uint64_t step, float *lr);
+
+/* Outlier detector ("04 · 多 GPU 与混合精度" §4: z-score of the grad norm
+ * over a window of 128 values; the update is skipped when it exceeds a
+ * threshold).  State lives in device memory so the decision never leaves
+ * the GPU.  bfo_outlier_update reads *value (device float, e.g.
+ * &norm_out->norm), and writes, on `stream`:
+ *   *z    = (value - mean) / sqrt(variance) of the previous `window` finite
+ *           values (binary64, population variance, summed oldest to newest),
+ *           NaN until `window` values have been seen;
+ *   *skip = 1 if value is not finite, or threshold > 0 and z > threshold;
+ *           else 0 (pass skip to adamw_sr_step);
+ * then appends value to the window if it is finite.  window: 1..4096. */
+typedef struct bfo_outlier_s *bfo_outlier;
+int bfo_outlier_create(uint32_t window, float threshold, bfo_outlier *out);
+int bfo_outlier_destroy(bfo_outlier detector);
+/* Empties the window (queued on `stream`). */
+int bfo_outlier_reset(bfo_outlier detector, void *stream);
+int bfo_outlier_update(bfo_outlier detector, const float *value, float *z, int32_t *skip, void *stream);
 
 /* Static string naming a status code. */
 const char *bfo_status_string(int status);

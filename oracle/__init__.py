@@ -73,6 +73,11 @@ def _load():
         "oracle_shard_map_per_tensor": (ctypes.c_int, [_vp, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                                        _vp, ctypes.c_uint64, _u64p]),
         "oracle_master_to_bf16_sr_mapped": (None, [_vp, _vp, ctypes.c_uint64, ctypes.c_uint64, _vp]),
+        "oracle_lr_at": (ctypes.c_float, [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float]),
+        "oracle_outlier_init": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32]),
+        "oracle_outlier_update": (None, [ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -240,3 +245,33 @@ def master_to_bf16_sr_mapped(M, gidx, seed, P_full):
     _need(M, np.float32, "M")
     _need(P_full, np.uint16, "P_full")
     _load().oracle_master_to_bf16_sr_mapped(_ptr(M), _ptr(gidx), gidx.size, seed, _ptr(P_full))
+
+
+LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
+
+
+def lr_at(kind, step, warmup, total, lr_max, final_frac=0.0, decay_frac=0.0):
+    return _load().oracle_lr_at(kind, step, warmup, total, lr_max, final_frac, decay_frac)
+
+
+class _OutlierState(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_uint32), ("count", ctypes.c_uint32), ("head", ctypes.c_uint32),
+                ("pad", ctypes.c_uint32), ("values", ctypes.c_float * 4096)]
+
+
+class Outlier:
+    """The oracle's z-score detector (window of previous finite values)."""
+
+    def __init__(self, window=128, threshold=0.0):
+        self._st = _OutlierState()
+        rc = _load().oracle_outlier_init(ctypes.byref(self._st), window)
+        if rc != OK:
+            raise ValueError(f"oracle_outlier_init failed: {rc}")
+        self.threshold = threshold
+
+    def update(self, x):
+        """Returns (z, skip) for value x, then appends x if finite."""
+        z = ctypes.c_float(0.0)
+        sk = ctypes.c_int32(0)
+        _load().oracle_outlier_update(ctypes.byref(self._st), x, self.threshold, ctypes.byref(z), ctypes.byref(sk))
+        return z.value, sk.value

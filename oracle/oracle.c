@@ -29,6 +29,7 @@
  * fmaf() calls, division and sqrtf are correctly rounded and subnormals are
  * kept.  Sums of squares are formed in binary64.
  */
+#define _DEFAULT_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -427,4 +428,87 @@ void oracle_master_to_bf16_sr_mapped(const float *M, const uint64_t *gidx, uint6
 /* Array helper for the test harness: widen bf16 patterns to binary32. */
 void oracle_bf16_to_f32_array(const uint16_t *h, uint64_t count, float *out) {
     for (uint64_t k = 0; k < count; ++k) out[k] = oracle_bf16_to_f32(h[k]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Step control: learning-rate schedules and the outlier z-score        */
+/* ------------------------------------------------------------------ */
+
+#define ORACLE_LR_CONSTANT 0
+#define ORACLE_LR_LINEAR 1
+#define ORACLE_LR_COSINE 2
+#define ORACLE_LR_WSD 3
+
+/* [LLMC] §4 names four schedules (cosine, linear, constant, wsd) without
+ * formulas; the readings, for 0-based step s, peak lr_max, floor
+ * lr_min = final_frac * lr_max, W warm-up steps and T total steps:
+ *   warm-up (s < W): lr_max * (s + 1) / W, for every kind;
+ *   afterwards, with progress p = (s - W) / (T - W) clamped to [0, 1]:
+ *   constant: lr_max;
+ *   linear:   lr_max - (lr_max - lr_min) * p;
+ *   cosine:   lr_min + (lr_max - lr_min) * (1 + cos(pi * p)) / 2;
+ *   wsd:      lr_max while s < T - D, then linear from lr_max to lr_min over
+ *             the last D = decay_frac * T steps (warm-up, stable, decay).
+ * Evaluated in binary64 and rounded once to binary32. */
+float oracle_lr_at(int kind, uint64_t step, uint64_t warmup, uint64_t total, float lr_max,
+                   float final_frac, float decay_frac) {
+    double peak = (double)lr_max;
+    double floor_lr = (double)final_frac * peak;
+    if (step < warmup) return (float)(peak * (double)(step + 1) / (double)warmup);
+    if (kind == ORACLE_LR_CONSTANT) return lr_max;
+    if (kind == ORACLE_LR_WSD) {
+        double decay_steps = (double)decay_frac * (double)total;
+        double decay_start = (double)total - decay_steps;
+        if ((double)step < decay_start || decay_steps <= 0.0) return lr_max;
+        double q = ((double)step - decay_start) / decay_steps;
+        if (q > 1.0) q = 1.0;
+        return (float)(peak - (peak - floor_lr) * q);
+    }
+    double span = (double)total - (double)warmup;
+    double p = span > 0.0 ? ((double)step - (double)warmup) / span : 1.0;
+    if (p > 1.0) p = 1.0;
+    if (kind == ORACLE_LR_LINEAR) return (float)(peak - (peak - floor_lr) * p);
+    return (float)(floor_lr + (peak - floor_lr) * (1.0 + cos(M_PI * p)) / 2.0);
+}
+
+/* [LLMC] §4: a z-score of the grad norm (or loss) over a window of the 128
+ * previous values; the update is skipped when it exceeds a threshold.
+ * Reading: mean and variance (population, divide by the window length) of
+ * the previous `window` finite values, summed in binary64 from oldest to
+ * newest; z = (x - mean) / sqrt(variance), NaN until the window is full;
+ * skip when x is not finite, or when threshold > 0 and z > threshold.  x
+ * then joins the window (oldest value dropped) unless it is not finite. */
+typedef struct {
+    uint32_t window, count, head, pad;
+    float values[4096];
+} oracle_outlier;
+
+int oracle_outlier_init(oracle_outlier *d, uint32_t window) {
+    if (window == 0 || window > 4096) return ORACLE_EINVAL;
+    memset(d, 0, sizeof *d);
+    d->window = window;
+    return ORACLE_OK;
+}
+
+void oracle_outlier_update(oracle_outlier *d, float x, float threshold, float *z_out, int32_t *skip_out) {
+    double z = NAN;
+    if (d->count == d->window) {
+        double sum = 0.0;
+        for (uint32_t k = 0; k < d->window; ++k) sum += (double)d->values[(d->head + k) % d->window];
+        double mean = sum / (double)d->window;
+        double sq = 0.0;
+        for (uint32_t k = 0; k < d->window; ++k) {
+            double dev = (double)d->values[(d->head + k) % d->window] - mean;
+            sq += dev * dev;
+        }
+        z = ((double)x - mean) / sqrt(sq / (double)d->window);
+    }
+    int finite = isfinite(x);
+    *z_out = (float)z;
+    *skip_out = (!finite || (threshold > 0.0f && z > (double)threshold)) ? 1 : 0;
+    if (finite) {
+        d->values[d->head] = x;
+        d->head = (d->head + 1) % d->window;
+        if (d->count < d->window) ++d->count;
+    }
 }

@@ -92,7 +92,8 @@ def test_entry_points_reject_null_table_and_bad_scalars(bfo):
     lib = bfo.library()
     hp = bfo.AdamwHParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
     assert lib.grad_global_norm(None, None, 1.0, None, None) == bfo.EINVAL
-    assert lib.adamw_sr_step(None, None, None, None, None, None, ctypes.byref(hp), None, 1, 0, 0, None) == bfo.EINVAL
+    assert lib.adamw_sr_step(None, None, None, None, None, None, ctypes.byref(hp), None, None, 1, 0, 0,
+                             None) == bfo.EINVAL
     assert lib.master_to_bf16_sr(None, None, None, 0, None) == bfo.EINVAL
     assert lib.bfo_decay_mask_dump(None, None, None) == bfo.EINVAL
     assert lib.bfo_table_info(None, None, None, None) == bfo.EINVAL
@@ -116,3 +117,17 @@ def test_binding_refuses_a_missing_library(tmp_path, monkeypatch):
         monkeypatch.undo()
         sys.modules.pop("bf16_numerics_amd.binding", None)
         importlib.import_module("bf16_numerics_amd.binding")
+
+
+def test_lr_schedule_library_matches_oracle(bfo):
+    import oracle as o
+    for kind in (bfo.LR_CONSTANT, bfo.LR_LINEAR, bfo.LR_COSINE, bfo.LR_WSD):
+        for (W_, T_, peak, frac, dfrac) in ((0, 100, 6e-4, 0.0, 0.25), (700, 18_865, 6e-4, 0.1, 0.2),
+                                           (5, 5, 1e-3, 0.5, 0.0)):
+            for s in list(range(0, 40)) + list(range(T_ - 40, T_ + 5)) + [T_ // 2, 10 ** 9]:
+                assert bfo.lr_at(kind, s, W_, T_, peak, frac, dfrac) == o.lr_at(kind, s, W_, T_, peak, frac, dfrac)
+    lib = bfo.library()
+    bad = bfo.LrSchedule(9, 0, 0, 10, 1e-3, 0.0, 0.0, 0)
+    assert lib.bfo_lr_at(ctypes.byref(bad), 0, ctypes.byref(ctypes.c_float())) == bfo.EINVAL
+    bad = bfo.LrSchedule(0, 0, 20, 10, 1e-3, 0.0, 0.0, 0)
+    assert lib.bfo_lr_at(ctypes.byref(bad), 0, ctypes.byref(ctypes.c_float())) == bfo.EINVAL

@@ -581,3 +581,87 @@ def test_update_per_tensor_gpt2_124m(bfo):
         assert_bf16_parity(u16(P), Ph, "per-tensor 124M params")
         for k in ("M", "m", "v"):
             assert_f32_parity(f32(st[k]), h[k], f"per-tensor 124M {k}")
+
+
+# --------------------------------------------------------------------- step control
+
+
+def test_outlier_detector_matches_oracle(bfo):
+    rs = np.random.default_rng(21)
+    window, thr = 32, 3.0
+    xs = list(rs.normal(8.0, 0.5, 160).astype(np.float32))
+    xs[70] = np.float32(80.0)
+    xs[90] = np.float32(np.inf)
+    xs[91] = np.float32(np.nan)
+    xs[120] = np.float32(8.0 + 2.9 * 0.5)
+    dev = bfo.Outlier(window, thr, device=DEV)
+    ref = o.Outlier(window, thr)
+    val = torch.zeros(1, dtype=torch.float32, device=DEV)
+    for k, x in enumerate(xs):
+        val.fill_(float(x))
+        dev.update(val)
+        z, skip = float(dev.z.item()), int(dev.skip.item())
+        rz, rskip = ref.update(float(x))
+        assert skip == rskip, (k, z, rz)
+        assert (math.isnan(z) and math.isnan(rz)) or np.float32(z).view(np.uint32) == np.float32(rz).view(np.uint32), \
+            (k, z, rz)
+    dev.reset()
+    val.fill_(100.0)
+    dev.update(val)
+    assert math.isnan(dev.z.item()) and dev.skip.item() == 0
+
+
+@pytest.mark.parametrize("master", [True, False])
+def test_skip_flag_freezes_the_step(bfo, master):
+    w = ragged_workload(3, 5)
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV, master=master)
+    W.fill_grads(torch, w, st["G"], 0, 1)
+    before = host_copy(st)
+    skip = torch.ones(1, dtype=torch.int32, device=DEV)
+    bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, 1, step_seed(1), skip=skip)
+    after = host_copy(st)
+    for k in ("P", "M", "m", "v"):
+        if before[k] is not None:
+            assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
+    skip.zero_()
+    bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, 1, step_seed(1), skip=skip)
+    oracle_step(o.table(w.entries()), 0, before, w.hparams, 1.0, 1, step_seed(1))
+    assert_state_parity(host_copy(st), before, "skip=0")
+
+
+def test_step_control_pipeline_skips_the_spike(bfo):
+    # norm -> detector(norm) -> update(skip) with no host round trip; a
+    # gradient spike at one step must be skipped, the others applied, and the
+    # trajectory must match the oracle driven by the same decisions.
+    w = ragged_workload(6, 3)
+    w.grad_std = 1e-3
+    ents = w.entries()
+    T = bfo.Table(ents)
+    tbl = o.table(ents)
+    st = device_state(w, 0, w.n, DEV)
+    h = host_copy(st)
+    res = bfo.new_norm_result(DEV)
+    det = bfo.Outlier(16, 5.0, device=DEV)
+    ref = o.Outlier(16, 5.0)
+    skipped = []
+    for t in range(1, 41):
+        lr = bfo.lr_at(bfo.LR_COSINE, t - 1, 5, 40, 1e-3, 0.1)
+        hp = W.HParams(lr=lr)
+        W.fill_grads(torch, w, st["G"], 0, t)
+        if t == 30:
+            st["G"].mul_(1000.0)
+        bfo.grad_global_norm(T, st["G"], res)
+        det.update(bfo.norm_ptr(res))
+        bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], hp, t, step_seed(t), scale=res,
+                          skip=det.skip)
+        _, norm, scale = bfo.read_norm_result(res)
+        _, rskip = ref.update(norm)
+        assert int(det.skip.item()) == rskip, t
+        if rskip:
+            skipped.append(t)
+            continue
+        h["G"] = u16(st["G"])
+        oracle_step(tbl, 0, h, hp, scale, t, step_seed(t))
+    assert skipped == [30]
+    assert_state_parity(host_copy(st), h, "step control")

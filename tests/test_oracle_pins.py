@@ -479,3 +479,58 @@ def test_per_tensor_sharded_steps_equal_unsharded():
         for gidx, Mr, _, _ in parts:
             o.master_to_bf16_sr_mapped(Mr, gidx, (1337 << 32) | 3, Pr)
         assert np.array_equal(Pr, P)
+
+
+# ---------------------------------------------------------------- step control
+
+
+def test_lr_schedule_closed_forms():
+    # Warm-up is linear to the peak; cosine passes the mid value at half
+    # progress and ends at the floor; linear is the straight line; WSD holds
+    # the peak until its decay tail; constant holds the peak.
+    W_, T_, frac = 10, 110, 0.1
+    peak = float(np.float32(1e-3))                       # lr_max is a binary32 argument
+    low = peak * float(np.float32(frac))
+    f32 = lambda x: float(np.float32(x))
+    for kind in (o.LR_CONSTANT, o.LR_LINEAR, o.LR_COSINE, o.LR_WSD):
+        assert o.lr_at(kind, 0, W_, T_, peak, frac, 0.2) == f32(peak / W_)
+        assert o.lr_at(kind, 4, W_, T_, peak, frac, 0.2) == f32(peak * 5 / W_)
+        assert o.lr_at(kind, W_ - 1, W_, T_, peak, frac, 0.2) == f32(peak)
+    assert o.lr_at(o.LR_COSINE, W_, W_, T_, peak, frac) == f32(peak)
+    assert abs(o.lr_at(o.LR_COSINE, 60, W_, T_, peak, frac) - (peak + low) / 2) <= 1e-7 * peak
+    assert abs(o.lr_at(o.LR_COSINE, T_, W_, T_, peak, frac) - low) <= 1e-7 * peak
+    assert abs(o.lr_at(o.LR_COSINE, 35, W_, T_, peak, frac) -
+               (low + (peak - low) * (1 + math.cos(math.pi / 4)) / 2)) <= 1e-7 * peak
+    assert abs(o.lr_at(o.LR_LINEAR, 60, W_, T_, peak, frac) - (peak + low) / 2) <= 1e-7 * peak
+    assert abs(o.lr_at(o.LR_LINEAR, 10_000, W_, T_, peak, frac) - low) <= 1e-7 * peak
+    assert o.lr_at(o.LR_CONSTANT, 10_000, W_, T_, peak, frac) == f32(peak)
+    # WSD with a 20% tail: plateau until step 88, then linear to the floor at 110
+    assert all(o.lr_at(o.LR_WSD, s, W_, T_, peak, frac, 0.2) == f32(peak) for s in range(W_, 88))
+    assert abs(o.lr_at(o.LR_WSD, 99, W_, T_, peak, frac, 0.2) - (peak + low) / 2) <= 1e-7 * peak
+    assert abs(o.lr_at(o.LR_WSD, 110, W_, T_, peak, frac, 0.2) - low) <= 1e-7 * peak
+
+
+def test_outlier_zscore_matches_numpy():
+    # z of each value against numpy's mean and population std of the previous
+    # `window` finite values; NaN before the window fills.
+    rs = np.random.default_rng(12)
+    window = 16
+    xs = list(rs.normal(5.0, 0.3, 80).astype(np.float32))
+    xs[40] = np.float32(50.0)            # a spike
+    xs[55] = np.float32(np.nan)          # a non-finite value
+    det = o.Outlier(window, threshold=4.0)
+    hist = []
+    for k, x in enumerate(xs):
+        z, skip = det.update(float(x))
+        if not np.isfinite(x):
+            assert skip == 1
+            continue
+        if len(hist) < window:
+            assert math.isnan(z) and skip == 0
+        else:
+            prev = np.array(hist[-window:], np.float64)
+            want = (float(x) - prev.mean()) / prev.std()
+            assert abs(z - want) <= 1e-6 * abs(want) + 1e-9, (k, z, want)
+            assert skip == (1 if want > 4.0 else 0)
+        hist.append(float(x))
+    assert det.update(50.0)[1] == 1 and o.Outlier(window, threshold=0.0).update(50.0)[1] == 0
