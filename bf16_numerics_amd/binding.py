@@ -20,6 +20,9 @@ EMISALIGNED = -4
 ETABLE = -5
 EHIP = -6
 EDEVICE = -7
+EIO = -8
+EFORMAT = -9
+ENOTFOUND = -10
 
 ROUND_SR = 0
 ROUND_RNE = 1
@@ -32,7 +35,8 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_table_info", "bfo_table_runs",
            "grad_global_norm", "adamw_sr_step", "master_to_bf16_sr", "bfo_rng_dump",
            "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error", "bfo_lr_at",
-           "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update")
+           "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
+           "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -98,6 +102,10 @@ def _lib():
         "bfo_outlier_destroy": (i32, [vp]),
         "bfo_outlier_reset": (i32, [vp, vp]),
         "bfo_outlier_update": (i32, [vp, vp, vp, vp, vp]),
+        "bfo_checkpoint_save": (i32, [ctypes.c_char_p, vp, vp, vp, vp, vp, u64, u64, vp]),
+        "bfo_checkpoint_done": (i32, [ctypes.c_char_p, u64]),
+        "bfo_checkpoint_latest": (i32, [ctypes.c_char_p, pu64]),
+        "bfo_checkpoint_load": (i32, [ctypes.c_char_p, u64, vp, vp, vp, vp, vp, pu64, vp]),
         "master_to_bf16_sr": (i32, [vp, vp, vp, u64, vp]),
         "bfo_rng_dump": (i32, [u64, u64, u64, vp, vp]),
         "bfo_decay_mask_dump": (i32, [vp, vp, vp]),
@@ -364,3 +372,43 @@ def decay_mask_dump(table):
         _check("bfo_decay_mask_dump", _lib().bfo_decay_mask_dump(table.handle, ctypes.c_void_p(out.data_ptr()),
                                                                  _stream(dev)))
     return out
+
+
+def checkpoint_save(directory, table, m, v, step, seed, master=None, params=None):
+    """Write this rank's state of `step` (master, or params when master is None)."""
+    dev = table.device
+    M = _arg(master, torch.float32, table.size, "master", dev)
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev) if master is None else None
+    mm = _arg(m, torch.float32, table.size, "m", dev)
+    vv = _arg(v, torch.float32, table.size, "v", dev)
+    with torch.cuda.device(dev):
+        _check("bfo_checkpoint_save", _lib().bfo_checkpoint_save(os.fsencode(directory), table.handle, p, M, mm, vv,
+                                                               step, seed, _stream(dev)))
+
+
+def checkpoint_done(directory, step):
+    _check("bfo_checkpoint_done", _lib().bfo_checkpoint_done(os.fsencode(directory), step))
+
+
+def checkpoint_latest(directory):
+    """Largest step with a DONE marker, or None."""
+    out = ctypes.c_uint64(0)
+    rc = _lib().bfo_checkpoint_latest(os.fsencode(directory), ctypes.byref(out))
+    if rc == ENOTFOUND:
+        return None
+    _check("bfo_checkpoint_latest", rc)
+    return out.value
+
+
+def checkpoint_load(directory, step, table, m, v, master=None, params=None):
+    """Read this rank's state of `step`; returns the saved seed."""
+    dev = table.device
+    M = _arg(master, torch.float32, table.size, "master", dev)
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev) if master is None else None
+    mm = _arg(m, torch.float32, table.size, "m", dev)
+    vv = _arg(v, torch.float32, table.size, "v", dev)
+    seed = ctypes.c_uint64(0)
+    with torch.cuda.device(dev):
+        _check("bfo_checkpoint_load", _lib().bfo_checkpoint_load(os.fsencode(directory), step, table.handle, p, M,
+                                                               mm, vv, ctypes.byref(seed), _stream(dev)))
+    return seed.value

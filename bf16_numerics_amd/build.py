@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbf16opt.so")
 SOURCES = [os.path.join(CSRC, "bfo_kernels.hip"), os.path.join(CSRC, "bfo_abi.cpp"),
-           os.path.join(CSRC, "bfo_control.cpp")]
+           os.path.join(CSRC, "bfo_control.cpp"), os.path.join(CSRC, "bfo_checkpoint.cpp")]
 ARCH = os.environ.get("BFO_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

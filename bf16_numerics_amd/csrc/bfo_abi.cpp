@@ -32,6 +32,7 @@ struct bfo_table_s {
     uint32_t world = 1, rank = 0;
     int layout = BFO_LAYOUT_FLAT;
     int device = 0;
+    uint64_t fingerprint = 0;        // FNV-1a over the tensor table
     std::vector<bfo_run> runs;       // host copy of the plan
     void *devBlock = nullptr;        // one allocation holding everything below
     uint32_t *tile = nullptr;        // [ntiles]
@@ -43,6 +44,10 @@ struct bfo_table_s {
 
     bfo::ShardView view() const { return {tile, local, addr, rng, flag}; }
 };
+
+bfo::TableFacts bfo::tableFacts(const bfo_table_s *t) {
+    return {t->n, t->S, t->world, t->rank, t->layout, t->fingerprint, t->runs.data(), uint32_t(t->runs.size())};
+}
 
 extern "C" {
 
@@ -135,8 +140,23 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
         tileWord[t] = uint32_t(k) | (local[k + 1] < t1 ? bfo::kTileMixed : 0u);
     }
 
+    // Fingerprint of the table, stored in checkpoints to refuse a mismatch.
+    uint64_t fp = 1469598103934665603ull;
+    auto mix = [&fp](uint64_t x) {
+        for (int byte = 0; byte < 8; ++byte) {
+            fp ^= (x >> (8 * byte)) & 0xFFu;
+            fp *= 1099511628211ull;
+        }
+    };
+    for (uint32_t t = 0; t < count; ++t) {
+        mix(tensors[t].offset);
+        mix(tensors[t].numel);
+        mix(tensors[t].flags);
+    }
+
     bfo_table_s *tb = new (std::nothrow) bfo_table_s;
     if (!tb) return BFO_EINVAL;
+    tb->fingerprint = fp;
     tb->n = n;
     tb->S = S;
     tb->begin = b;
@@ -315,6 +335,9 @@ const char *bfo_status_string(int status) {
         case BFO_ETABLE: return "tensor table not contiguous from 0 or undefined flag bits";
         case BFO_EHIP: return "HIP runtime call failed";
         case BFO_EDEVICE: return "current device differs from the table's device";
+        case BFO_EIO: return "file could not be created, written or read";
+        case BFO_EFORMAT: return "checkpoint file does not match the table or is incomplete";
+        case BFO_ENOTFOUND: return "no such checkpoint";
         default: return "unknown status";
     }
 }

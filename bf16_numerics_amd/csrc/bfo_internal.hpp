@@ -58,6 +58,17 @@ struct StepScalars {
 // Records a failed HIP call for bfo_last_hip_error() and returns BFO_EHIP.
 int recordHipFailure(hipError_t e);
 
+// What the checkpoint code needs to know about a table (bfo_abi.cpp).
+struct TableFacts {
+    uint64_t n, S;
+    uint32_t world, rank;
+    int layout;
+    uint64_t fingerprint;  // FNV-1a over every tensor's offset, numel and flags
+    const bfo_run *runs;
+    uint32_t nruns;
+};
+TableFacts tableFacts(const bfo_table_s *table);
+
 // Launchers (bfo_kernels.hip).  Shapes are checked by the caller: M, m, v
 // hold S shard-local elements, 16-byte aligned; P and G are addressed
 // through the runs and are at least 2-byte aligned; pgVec says whether P

@@ -68,7 +68,10 @@ enum {
     BFO_EMISALIGNED = -4,   /* pointer not aligned as required (see Memory above) */
     BFO_ETABLE = -5,        /* table not contiguous from 0, or undefined flag bits set */
     BFO_EHIP = -6,          /* a HIP runtime call failed */
-    BFO_EDEVICE = -7        /* called with a different current device than the table's */
+    BFO_EDEVICE = -7,       /* called with a different current device than the table's */
+    BFO_EIO = -8,           /* a checkpoint file could not be created, written or read */
+    BFO_EFORMAT = -9,       /* a checkpoint file does not match the table, or is truncated */
+    BFO_ENOTFOUND = -10     /* no such checkpoint (file or DONE marker) */
 };
 
 enum { BFO_ROUND_SR = 0, BFO_ROUND_RNE = 1 };
@@ -263,6 +266,40 @@ int bfo_outlier_destroy(bfo_outlier detector);
 /* Empties the window (queued on `stream`). */
 int bfo_outlier_reset(bfo_outlier detector, void *stream);
 int bfo_outlier_update(bfo_outlier detector, const float *value, float *z, int32_t *skip, void *stream);
+
+/* Checkpoints ("04 · 多 GPU 与混合精度" §5.1-5.2).  Each rank saves its own
+ * optimizer state; a DONE marker written after every rank has saved makes
+ * the checkpoint count; resume takes the newest step with a marker.  The
+ * bf16 weights are not saved when there is a master: after loading, call
+ * master_to_bf16_sr(table, master, params, seed) with the returned seed and
+ * they come back bit-identical to the ones the saved step produced.
+ *
+ * bfo_checkpoint_save writes <dir>/state_<step:08>_<rank:05>.bin: a 96-byte
+ * header (magic "BFOSTATE", version 1, step, seed, n, S, world, rank,
+ * layout, whether a master is stored, and a fingerprint of the tensor table)
+ * and the payload master (S fp32) -- or, when master is NULL, the shard's
+ * bf16 params in shard-local order (params addressed as in adamw_sr_step) --
+ * then m and v (S fp32 each).  step is the last step the state includes and
+ * seed the rounding seed of its update.  Device arrays are copied through a
+ * pinned buffer on `stream` after the work already queued there; the call
+ * returns when the file is on disk (written under a temporary name, synced,
+ * then renamed).  Errors: BFO_EINVAL, BFO_EIO, BFO_EHIP. */
+int bfo_checkpoint_save(const char *dir, bfo_table table, const uint16_t *params, const float *master,
+                        const float *m, const float *v, uint64_t step, uint64_t seed, void *stream);
+
+/* Creates the empty marker <dir>/DONE_<step:08>. */
+int bfo_checkpoint_done(const char *dir, uint64_t step);
+
+/* *step = the largest step with a DONE marker in dir; BFO_ENOTFOUND if none. */
+int bfo_checkpoint_latest(const char *dir, uint64_t *step);
+
+/* Reads this rank's state of `step` into master (or, when master is NULL,
+ * into the shard's positions of params), m and v; *seed (if not NULL) gets
+ * the saved seed.  BFO_ENOTFOUND if the file is missing; BFO_EFORMAT if its
+ * header does not match the table (sizes, world, rank, layout, fingerprint,
+ * master or not) or the file is truncated. */
+int bfo_checkpoint_load(const char *dir, uint64_t step, bfo_table table, uint16_t *params, float *master,
+                        float *m, float *v, uint64_t *seed, void *stream);
 
 /* Static string naming a status code. */
 const char *bfo_status_string(int status);

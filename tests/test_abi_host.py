@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(bfo):
 
 def test_status_strings(bfo):
     lib = bfo.library()
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
         s = lib.bfo_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.bfo_status_string(-99).decode() == "unknown status"
@@ -131,3 +131,20 @@ def test_lr_schedule_library_matches_oracle(bfo):
     assert lib.bfo_lr_at(ctypes.byref(bad), 0, ctypes.byref(ctypes.c_float())) == bfo.EINVAL
     bad = bfo.LrSchedule(0, 0, 20, 10, 1e-3, 0.0, 0.0, 0)
     assert lib.bfo_lr_at(ctypes.byref(bad), 0, ctypes.byref(ctypes.c_float())) == bfo.EINVAL
+
+
+def test_checkpoint_latest_reads_done_markers(bfo, tmp_path):
+    d = str(tmp_path)
+    assert bfo.checkpoint_latest(d) is None
+    for name in ("state_00000012_00000.bin", "DONE_x", "DONE_", "DONEX_00000099", "DONE_00000003"):
+        (tmp_path / name).write_bytes(b"")
+    assert bfo.checkpoint_latest(d) == 3
+    bfo.checkpoint_done(d, 12)
+    assert (tmp_path / "DONE_00000012").exists()
+    assert bfo.checkpoint_latest(d) == 12
+    lib = bfo.library()
+    assert lib.bfo_checkpoint_latest(os.fsencode(str(tmp_path / "missing")), ctypes.byref(ctypes.c_uint64())) == bfo.EIO
+    assert lib.bfo_checkpoint_latest(None, None) == bfo.EINVAL
+    assert lib.bfo_checkpoint_done(None, 1) == bfo.EINVAL
+    assert lib.bfo_checkpoint_save(b"/tmp", None, None, None, None, None, 1, 1, None) == bfo.EINVAL
+    assert lib.bfo_checkpoint_load(b"/tmp", 1, None, None, None, None, None, None, None) == bfo.EINVAL

@@ -665,3 +665,85 @@ def test_step_control_pipeline_skips_the_spike(bfo):
         oracle_step(tbl, 0, h, hp, scale, t, step_seed(t))
     assert skipped == [30]
     assert_state_parity(host_copy(st), h, "step control")
+
+
+# --------------------------------------------------------------------- checkpoint / resume
+
+
+def test_checkpoint_resume_is_bit_exact(bfo, tmp_path):
+    # "04 · 多 GPU 与混合精度" §5.2: resume from (master, m, v, last seed),
+    # rebuild the bf16 weights with the last update's draws, and the run
+    # continues bit-identically to one that never stopped.
+    w = ragged_workload(6, 3)
+    w.grad_std = 0.05
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV)
+    res = bfo.new_norm_result(DEV)
+
+    def step(state, t):
+        W.fill_grads(torch, w, state["G"], 0, t)
+        bfo.grad_global_norm(T, state["G"], res)
+        bfo.adamw_sr_step(T, state["P"], state["G"], state["M"], state["m"], state["v"], w.hparams, t,
+                          step_seed(t), scale=res)
+
+    for t in range(1, 5):
+        step(st, t)
+    P4 = st["P"].clone()
+    d = str(tmp_path)
+    bfo.checkpoint_save(d, T, st["m"], st["v"], 4, step_seed(4), master=st["M"])
+    assert bfo.checkpoint_latest(d) is None            # not done until marked
+    bfo.checkpoint_done(d, 4)
+    for t in range(5, 9):
+        step(st, t)
+    want = host_copy(st)
+
+    fresh = {"P": torch.empty_like(st["P"]), "M": torch.empty_like(st["M"]), "m": torch.empty_like(st["m"]),
+             "v": torch.empty_like(st["v"]), "G": torch.empty_like(st["G"])}
+    last = bfo.checkpoint_latest(d)
+    assert last == 4
+    seed = bfo.checkpoint_load(d, last, T, fresh["m"], fresh["v"], master=fresh["M"])
+    assert seed == step_seed(4)
+    bfo.master_to_bf16_sr(T, fresh["M"], fresh["P"], seed)
+    assert torch.equal(fresh["P"].view(torch.int16), P4.view(torch.int16))
+    for t in range(5, 9):
+        step(fresh, t)
+    got = host_copy(fresh)
+    for k in ("P", "M", "m", "v"):
+        assert np.array_equal(got[k].view(np.uint8), want[k].view(np.uint8)), k
+
+
+def test_checkpoint_no_master_per_tensor_round_trip_and_errors(bfo, tmp_path):
+    w = W.tiny()
+    ents = w.entries()
+    world, r = 4, 2
+    T = bfo.Table(ents, world, r, layout=bfo.LAYOUT_PER_TENSOR)
+    P, _, _, _ = W.init_state(torch, w, 0, w.n, DEV, master=False)
+    m = torch.randn(T.size, device=DEV)
+    v = torch.rand(T.size, device=DEV)
+    d = str(tmp_path)
+    bfo.checkpoint_save(d, T, m, v, 7, 99, params=P)
+    P2 = torch.zeros_like(P)
+    m2, v2 = torch.empty_like(m), torch.empty_like(v)
+    assert bfo.checkpoint_load(d, 7, T, m2, v2, params=P2) == 99
+    gi = torch.from_numpy(T.global_index().astype(np.int64)).to(DEV)
+    assert torch.equal(P2[gi].view(torch.int16), P[gi].view(torch.int16))
+    mask = torch.ones(w.n, dtype=torch.bool, device=DEV)
+    mask[gi] = False
+    assert not bool(P2.view(torch.int16)[mask].any())    # only this rank's elements were written
+    assert torch.equal(m2, m) and torch.equal(v2, v)
+    # refusals: another rank's table, a master where none was saved, a missing step, a truncated file
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.checkpoint_load(d, 7, bfo.Table(ents, world, r, layout=bfo.LAYOUT_FLAT), m2, v2, params=P2[:T.size])
+    assert e.value.status == bfo.EFORMAT
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.checkpoint_load(d, 7, T, m2, v2, master=torch.empty_like(m))
+    assert e.value.status == bfo.EFORMAT
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.checkpoint_load(d, 8, T, m2, v2, params=P2)
+    assert e.value.status == bfo.ENOTFOUND
+    path = tmp_path / "state_00000007_00002.bin"
+    data = path.read_bytes()
+    path.write_bytes(data[:-4])
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.checkpoint_load(d, 7, T, m2, v2, params=P2)
+    assert e.value.status == bfo.EFORMAT
