@@ -6,13 +6,15 @@ through the C ABI on torch's current stream.  Inputs (state and a small pool
 of pre-generated gradient buffers) are resident in HBM before timing starts.
 
 Prints one JSON line: Gparams/s of the whole step, the HBM roofline of the
-dominant kernel (the update, 28 algorithmic bytes per parameter), and the CPU
-oracle timed on a bounded sample of the same workload.
+dominant kernel (the update, 28 algorithmic bytes per parameter), the CPU
+oracle timed on a bounded sample of the same workload, and an achievable
+ceiling: a kernel that moves the update's bytes with none of its arithmetic.
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -45,9 +47,21 @@ def measured_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+def cpu_threads():
+    """Host threads this process may use (the CPU share, not the machine)."""
+    k = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(k, int(cap))) if cap and cap.isdigit() else k
+
+
 def cpu_baseline(torch, w, st, begin, target_s):
-    """The oracle, as it stands, on a contiguous slice of the same shard:
-    grad norm + AdamW/SR update per step, one thread."""
+    """The oracle, as it stands, on a contiguous slice of the same shard: grad
+    norm + AdamW/SR update per step, first on one thread, then on K threads
+    (a static contiguous partition of the slice; each thread calls the oracle
+    on its part, and the per-part sums of squares are added in part order
+    before the clip scale).  The oracle's C functions run without the GIL."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle as o
     from bf16_numerics_amd import workloads as W
@@ -58,19 +72,56 @@ def cpu_baseline(torch, w, st, begin, target_s):
     tbl = o.table(w.entries())
     hp = o.hparams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
                    w.hparams.weight_decay, w.hparams.bias_correction)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        steps += 1
-        _, _, scale = o.grad_norm(h["G"], w.hparams.max_norm)
-        o.adamw_step(tbl, begin, h["P"], h["G"], h["M"], h["m"], h["v"], hp, scale, steps,
-                     (1337 << 32) | steps, o.ROUND_SR)
-        el = time.perf_counter() - t0
-        if el >= target_s or steps >= 64:
-            break
-    return {"value": count * steps / el / 1e9, "unit": "Gparams/s", "cores": 1, "kind": "oracle",
-            "sample": f"contiguous {count}-element slice of the {w.name} shard, {steps} steps of "
-                      f"grad norm + AdamW/SR update, {el:.1f} s single-threaded"}
+    max_norm = w.hparams.max_norm
+
+    def run(parts, pool, budget, first_step):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            steps += 1
+            t = first_step + steps
+            sums = list(pool.map(lambda r: o.grad_norm(h["G"][r[0]:r[1]], max_norm)[0], parts))
+            norm = float(np.float32(np.sqrt(sum(sums))))
+            scale = float(np.float32(max_norm / norm)) if norm > max_norm else 1.0
+            list(pool.map(lambda r: o.adamw_step(tbl, begin + r[0], h["P"][r[0]:r[1]], h["G"][r[0]:r[1]],
+                                                 h["M"][r[0]:r[1]], h["m"][r[0]:r[1]], h["v"][r[0]:r[1]], hp,
+                                                 scale, t, (1337 << 32) | t, o.ROUND_SR), parts))
+            el = time.perf_counter() - t0
+            if el >= budget or steps >= 256:
+                return steps, el
+
+    with ThreadPoolExecutor(1) as pool:
+        s1, el1 = run([(0, count)], pool, target_s / 2, 0)
+    k = cpu_threads()
+    cuts = [count * i // k // 8 * 8 for i in range(k)] + [count]
+    with ThreadPoolExecutor(k) as pool:
+        sk, elk = run(list(zip(cuts[:-1], cuts[1:])), pool, target_s / 2, s1)
+    one = count * s1 / el1 / 1e9
+    return {"value": count * sk / elk / 1e9, "unit": "Gparams/s", "cores": k, "kind": "oracle",
+            "sample": f"contiguous {count}-element slice of the {w.name} shard, grad norm + AdamW/SR update "
+                      f"per step: {sk} steps in {elk:.1f} s on {k} threads (static contiguous partition); "
+                      f"before that {s1} steps in {el1:.1f} s on 1 thread",
+            "single_thread_value": one}
+
+
+def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs):
+    """Achievable bandwidth for the update's own traffic on this device: the
+    library's stream-mix kernel (same 14 B read + 14 B written per element in
+    the update's vector and workgroup plan, no arithmetic; key 0 leaves m, v
+    and the master unchanged and copies G into P), timed per launch with HIP
+    events on the launch stream, as the update is."""
+    for _ in range(2):
+        bfo.stream_mix(P, G, M, m, v, 0)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, z in evs:
+        a.record(stream)
+        bfo.stream_mix(P, G, M, m, v, 0)
+        z.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(z) for a, z in evs) / launches
+    gbs = UPDATE_BYTES * M.numel() / (ms * 1e-3) / 1e9
+    return {"kernel": "streamMixKernel (update traffic, no arithmetic)", "achieved": round(gbs, 1),
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms, 5),
+            "update_over_ceiling": round(update_gbs / gbs, 4)}
 
 
 def main():
@@ -86,6 +137,8 @@ def main():
                     help="append a 1-D tensor of this many elements (e.g. 8 makes n/8 odd: misaligned shards)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the same-traffic streaming kernel timed after the step (achievable ceiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy 2 GiB -> 2 GiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -141,6 +194,8 @@ def main():
 
     def step(t, ev=None):
         G = pool[(t - 1) % len(pool)]
+        if ev is not None:
+            ev[2].record(stream)
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
         if ev is not None:
             ev[0].record(stream)
@@ -169,13 +224,14 @@ def main():
     # Per-launch duration of the dominant kernel (the update): K more steps with
     # HIP events recorded on the launch stream around each update call.  Kept
     # out of the region above because each event adds a few microseconds of gap.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     for k in range(args.steps):
         step(args.warmup + args.steps + 1 + k, evs[k])
     torch.cuda.synchronize()
-    upd_ms = [a.elapsed_time(z) for a, z in evs]
+    upd_ms = [a.elapsed_time(z) for a, z, _ in evs]
     upd_avg = sum(upd_ms) / len(upd_ms)
+    norm_ms = [s0.elapsed_time(a) for a, _, s0 in evs]
+    step_ev_ms = sorted(s0.elapsed_time(z) for _, z, s0 in evs)
     gparams = S / (ms_step * 1e-3) / 1e9
     step_gbs = (UPDATE_BYTES + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
     achieved = UPDATE_BYTES * S / (upd_avg * 1e-3) / 1e9
@@ -206,6 +262,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": UPDATE_BYTES * S,
                      "update_ms_avg": round(upd_avg, 5)},
+        "step_ms_events": {"mean": round(sum(step_ev_ms) / len(step_ev_ms), 5),
+                           "median": round(statistics.median(step_ev_ms), 5),
+                           "min": round(step_ev_ms[0], 5), "max": round(step_ev_ms[-1], 5),
+                           "norm_mean": round(sum(norm_ms) / len(norm_ms), 5)},
         "last_norm": {"norm": norm, "scale": scale},
     }
     if args.copy_calibration:
@@ -219,6 +279,8 @@ def main():
     if not args.no_cpu_baseline and args.layout == "flat":
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
         out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds)
+    if not args.no_ceiling:
+        out["ceiling"] = stream_ceiling(torch, bfo, stream, P[:S], pool[0][:S], M, m, v, args.steps, achieved)
     print(json.dumps(out), flush=True)
 
 

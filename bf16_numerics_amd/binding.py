@@ -36,7 +36,8 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "grad_global_norm", "adamw_sr_step", "master_to_bf16_sr", "bfo_rng_dump",
            "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error", "bfo_lr_at",
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
-           "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load")
+           "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
+           "bfo_stream_mix")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -109,6 +110,7 @@ def _lib():
         "master_to_bf16_sr": (i32, [vp, vp, vp, u64, vp]),
         "bfo_rng_dump": (i32, [u64, u64, u64, vp, vp]),
         "bfo_decay_mask_dump": (i32, [vp, vp, vp]),
+        "bfo_stream_mix": (i32, [vp, vp, vp, vp, vp, u64, u32, vp]),
         "bfo_status_string": (ctypes.c_char_p, [i32]),
         "bfo_last_hip_error": (i32, []),
     }
@@ -372,6 +374,19 @@ def decay_mask_dump(table):
         _check("bfo_decay_mask_dump", _lib().bfo_decay_mask_dump(table.handle, ctypes.c_void_p(out.data_ptr()),
                                                                  _stream(dev)))
     return out
+
+
+def stream_mix(params, grads, master, m, v, key=0):
+    """The update's memory traffic without its arithmetic (bandwidth ceiling).
+
+    m, v, master ^= key as bit patterns; params = grads ^ (key & 0xFFFF)."""
+    count = master.numel()
+    dev = master.device
+    args = [_arg(params, torch.bfloat16, count, "params", dev), _arg(grads, torch.bfloat16, count, "grads", dev),
+            _arg(master, torch.float32, count, "master", dev), _arg(m, torch.float32, count, "m", dev),
+            _arg(v, torch.float32, count, "v", dev)]
+    with torch.cuda.device(dev):
+        _check("bfo_stream_mix", _lib().bfo_stream_mix(*args, count, key & 0xFFFFFFFF, _stream(dev)))
 
 
 def checkpoint_save(directory, table, m, v, step, seed, master=None, params=None):

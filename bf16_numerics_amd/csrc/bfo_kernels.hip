@@ -324,6 +324,60 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
 }
 
 // ---------------------------------------------------------------------------
+// Measurement kernel: the update's memory traffic without its arithmetic.
+// Same tile, lane and vector plan as the 16-byte path of adamwTileKernel
+// (reads G, m, v, M; writes m, v, M, P), with each output a bit-XOR of its
+// input and a key, so that nothing can be elided and key 0 leaves m, v, M
+// bitwise as they were and copies G into P.  Its bandwidth is the ceiling the
+// update can reach on a given device.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__ P, const uint16_t *__restrict__ G,
+                                                          float *__restrict__ M, float *__restrict__ Mom,
+                                                          float *__restrict__ Var, uint64_t count, uint32_t key,
+                                                          uint64_t tileBase) {
+    const uint64_t tile = tileBase + blockIdx.x;
+    uint4 gv[kVecPerLane], ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
+    uint4 wa[kVecPerLane], wb[kVecPerLane];
+    int mode[kVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        mode[k] = q * 8 + 8 <= count ? kRegular : (q * 8 < count ? kPerElement : kNone);
+        if (mode[k] != kRegular) continue;
+        gv[k] = reinterpret_cast<const uint4 *>(G)[q];
+        ma[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q];
+        mb[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q + 1];
+        va[k] = reinterpret_cast<const uint4 *>(Var)[2 * q];
+        vb[k] = reinterpret_cast<const uint4 *>(Var)[2 * q + 1];
+        wa[k] = reinterpret_cast<const uint4 *>(M)[2 * q];
+        wb[k] = reinterpret_cast<const uint4 *>(M)[2 * q + 1];
+    }
+    const uint32_t key2 = (key & 0xFFFFu) | (key << 16);
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (mode[k] == kPerElement) {
+            for (uint64_t j = q * 8; j < count; ++j) {
+                Mom[j] = __uint_as_float(__float_as_uint(Mom[j]) ^ key);
+                Var[j] = __uint_as_float(__float_as_uint(Var[j]) ^ key);
+                M[j] = __uint_as_float(__float_as_uint(M[j]) ^ key);
+                P[j] = uint16_t(G[j] ^ key);
+            }
+            continue;
+        }
+        if (mode[k] != kRegular) continue;
+        const uint4 kk = make_uint4(key, key, key, key);
+        reinterpret_cast<uint4 *>(Mom)[2 * q] = ma[k] ^ kk;
+        reinterpret_cast<uint4 *>(Mom)[2 * q + 1] = mb[k] ^ kk;
+        reinterpret_cast<uint4 *>(Var)[2 * q] = va[k] ^ kk;
+        reinterpret_cast<uint4 *>(Var)[2 * q + 1] = vb[k] ^ kk;
+        reinterpret_cast<uint4 *>(M)[2 * q] = wa[k] ^ kk;
+        reinterpret_cast<uint4 *>(M)[2 * q + 1] = wb[k] ^ kk;
+        reinterpret_cast<uint4 *>(P)[q] = gv[k] ^ make_uint4(key2, key2, key2, key2);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Rebuild bf16 weights from the master: P = SR(M, draw), same vector plan.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
@@ -433,10 +487,15 @@ __device__ __forceinline__ double blockSum(double x) {
     return total;
 }
 
+// Workgroups take tiles from the shard's end backwards: the partial of a tile
+// depends only on its index, so the order changes no bit of the result, and the
+// lines read last (the shard's start) are the ones the update, which walks
+// forward, reads first while they may still sit in the memory-side cache.
 __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G, uint64_t S,
                                                            ShardView sv, int pgVec,
-                                                           double *__restrict__ partials, uint64_t tileBase) {
-    const uint64_t tile = tileBase + blockIdx.x;
+                                                           double *__restrict__ partials, uint64_t tileBase,
+                                                           uint64_t lastTile) {
+    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
     uint4 x[kNormVecPerLane];
     Place pl[kNormVecPerLane];
     int mode[kNormVecPerLane];
@@ -619,7 +678,7 @@ hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, fl
     for (uint64_t base = 0; base < ntiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = ntiles - base < kMaxBlocksPerLaunch ? ntiles - base : kMaxBlocksPerLaunch;
         hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, S, sv, pgVec,
-                           partials, base);
+                           partials, base, ntiles - 1);
     }
     const double *finishIn = partials;
     uint64_t finishCount = ntiles;
@@ -668,6 +727,17 @@ hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
         hipLaunchKernelGGL(masterToBf16Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P, S, sv, pgVec,
                            k0, k1, base);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launchStreamMix(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t count,
+                           uint32_t key, hipStream_t stream) {
+    const uint64_t tiles = (count + kTileElems - 1) / kTileElems;
+    for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
+        const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL(streamMixKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m, v, count, key,
+                           base);
     }
     return hipGetLastError();
 }

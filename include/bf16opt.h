@@ -223,6 +223,18 @@ int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, v
  * else 0, as the update kernel sees it (device array of S bytes). */
 int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
 
+/* Measurement export: the update's memory traffic with none of its
+ * arithmetic, for an achievable-bandwidth ceiling measured the same way as
+ * the update.  For j < count (device arrays of count elements):
+ *   m[j], v[j], master[j] ^= key (as 32-bit patterns); params[j] = grads[j] ^
+ *   (key & 0xFFFF).
+ * Reads 14 and writes 14 bytes per element, in the update's 16-byte vector
+ * and workgroup plan.  key 0 leaves m, v and master unchanged and copies
+ * grads into params.  All five pointers 16-byte aligned (else
+ * BFO_EMISALIGNED); count 0 is a no-op. */
+int bfo_stream_mix(uint16_t *params, const uint16_t *grads, float *master, float *m, float *v, uint64_t count,
+                   uint32_t key, void *stream);
+
 /* Learning-rate schedules ("04 · 多 GPU 与混合精度" §4 names cosine, linear,
  * constant and wsd; the formulas are this library's reading).  For 0-based
  * step s, lr_min = final_frac * lr_max, W = warmup_steps, T = total_steps:
