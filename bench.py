@@ -23,7 +23,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 UPDATE_BYTES = 28              # G 2 + m 4+4 + v 4+4 + M 4+4 + P 2 per parameter
+UPDATE_BYTES_NO_MASTER = 22    # G 2 + P 2+2 + m 4+4 + v 4+4
 NORM_BYTES = 2                 # G read once
+REBUILD_BYTES = 6              # master_to_bf16_sr: M 4 read + P 2 written
 METRIC = "optimizer Gparams/s per step + achieved HBM GB/s (% of peak), 1 MI355X"
 
 
@@ -54,9 +56,9 @@ def cpu_threads():
     return max(1, min(k, int(cap))) if cap and cap.isdigit() else k
 
 
-def cpu_baseline(torch, w, st, begin, target_s):
+def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
     """The oracle, as it stands, on a contiguous slice of the same shard: grad
-    norm + AdamW/SR update per step, first on one thread, then on K threads
+    norm + the timed AdamW variant per step, first on one thread, then on K threads
     (a static contiguous partition of the slice; each thread calls the oracle
     on its part, and the per-part sums of squares are added in part order
     before the clip scale).  The oracle's C functions run without the GIL."""
@@ -67,8 +69,10 @@ def cpu_baseline(torch, w, st, begin, target_s):
     from bf16_numerics_amd import workloads as W
 
     count = min(1 << 23, st["P"].numel())
-    h = {k: (W.bf16_bits_numpy(torch, t[:count]).copy() if t.dtype == torch.bfloat16
+    h = {k: (None if t is None else W.bf16_bits_numpy(torch, t[:count]).copy() if t.dtype == torch.bfloat16
              else t[:count].cpu().numpy().copy()) for k, t in st.items()}
+    rounding = o.ROUND_SR if rounding_sr else o.ROUND_RNE
+    sl = (lambda a, r: None if a is None else a[r[0]:r[1]])
     tbl = o.table(w.entries())
     hp = o.hparams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
                    w.hparams.weight_decay, w.hparams.bias_correction)
@@ -83,8 +87,8 @@ def cpu_baseline(torch, w, st, begin, target_s):
             norm = float(np.float32(np.sqrt(sum(sums))))
             scale = float(np.float32(max_norm / norm)) if norm > max_norm else 1.0
             list(pool.map(lambda r: o.adamw_step(tbl, begin + r[0], h["P"][r[0]:r[1]], h["G"][r[0]:r[1]],
-                                                 h["M"][r[0]:r[1]], h["m"][r[0]:r[1]], h["v"][r[0]:r[1]], hp,
-                                                 scale, t, (1337 << 32) | t, o.ROUND_SR), parts))
+                                                 sl(h["M"], r), h["m"][r[0]:r[1]], h["v"][r[0]:r[1]], hp,
+                                                 scale, t, (1337 << 32) | t, rounding), parts))
             el = time.perf_counter() - t0
             if el >= budget or steps >= 256:
                 return steps, el
@@ -97,10 +101,30 @@ def cpu_baseline(torch, w, st, begin, target_s):
         sk, elk = run(list(zip(cuts[:-1], cuts[1:])), pool, target_s / 2, s1)
     one = count * s1 / el1 / 1e9
     return {"value": count * sk / elk / 1e9, "unit": "Gparams/s", "cores": k, "kind": "oracle",
-            "sample": f"contiguous {count}-element slice of the {w.name} shard, grad norm + AdamW/SR update "
+            "sample": f"contiguous {count}-element slice of the {w.name} shard, grad norm + AdamW update "
+                      f"({'master' if h['M'] is not None else 'no master'}, {'SR' if rounding_sr else 'RNE'}) "
                       f"per step: {sk} steps in {elk:.1f} s on {k} threads (static contiguous partition); "
                       f"before that {s1} steps in {el1:.1f} s on 1 thread",
             "single_thread_value": one}
+
+
+def rebuild_rate(torch, bfo, stream, T, M, P, seed, launches):
+    """master_to_bf16_sr (the resume-time rebuild, 6 B per parameter) timed per
+    launch with HIP events on the launch stream.  It rewrites P from the
+    master with the last update's seed (after an SR update, the same bits)."""
+    for _ in range(2):
+        bfo.master_to_bf16_sr(T, M, P, seed)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, z in evs:
+        a.record(stream)
+        bfo.master_to_bf16_sr(T, M, P, seed)
+        z.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(z) for a, z in evs) / launches
+    gbs = REBUILD_BYTES * M.numel() / (ms * 1e-3) / 1e9
+    return {"kernel": "masterToBf16Kernel", "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms, 5),
+            "algorithmic_bytes_per_launch": REBUILD_BYTES * M.numel()}
 
 
 def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs):
@@ -135,6 +159,10 @@ def main():
                     help="ZeRO-1 shard layout: contiguous range, or 1/N of every tensor")
     ap.add_argument("--pad", type=int, default=0,
                     help="append a 1-D tensor of this many elements (e.g. 8 makes n/8 odd: misaligned shards)")
+    ap.add_argument("--no-master", action="store_true",
+                    help="time the no-master update (old weights read from the bf16 params, 22 B/param)")
+    ap.add_argument("--rounding", choices=("sr", "rne"), default="sr",
+                    help="bf16 write-back: stochastic (default) or round to nearest even")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -164,9 +192,9 @@ def main():
     if layout == bfo.LAYOUT_PER_TENSOR:
         # llm.c-style ZeRO-1: full-length bf16 params and grads, shard-local
         # fp32 master/m/v for this rank's 1/N of every tensor.
-        P, M_full, _, _ = W.init_state(torch, w, 0, w.n, dev)
+        P, M_full, _, _ = W.init_state(torch, w, 0, w.n, dev, master=not args.no_master)
         gi = torch.from_numpy(T.global_index().astype("int64")).to(dev)
-        M = M_full[gi].clone()
+        M = None if args.no_master else M_full[gi].clone()
         del M_full, gi
         m = torch.zeros(S, dtype=torch.float32, device=dev)
         v = torch.zeros(S, dtype=torch.float32, device=dev)
@@ -176,7 +204,7 @@ def main():
         # Contiguous ZeRO-1 layout: full-length bf16 params, shard-local rest.
         b, e = T.begin, T.end
         P_full = torch.empty(w.n if w.world > 1 else 0, dtype=torch.bfloat16, device=dev)
-        P, M, m, v = W.init_state(torch, w, b, e, dev)
+        P, M, m, v = W.init_state(torch, w, b, e, dev, master=not args.no_master)
         if w.world > 1:
             P_full[b:e] = P
             del P
@@ -191,6 +219,9 @@ def main():
     hp = bfo.AdamwHParams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
                           w.hparams.weight_decay, 1)
     stream = torch.cuda.current_stream(dev)
+    rounding = bfo.ROUND_RNE if args.rounding == "rne" else bfo.ROUND_SR
+    upd_bytes = UPDATE_BYTES_NO_MASTER if args.no_master else UPDATE_BYTES
+    variant = ("no-master" if args.no_master else "master") + "," + args.rounding.upper()
 
     def step(t, ev=None):
         G = pool[(t - 1) % len(pool)]
@@ -199,7 +230,7 @@ def main():
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
         if ev is not None:
             ev[0].record(stream)
-        bfo.adamw_sr_step(T, P, G, M, m, v, hp, t, (1337 << 32) | t, scale=res)
+        bfo.adamw_sr_step(T, P, G, M, m, v, hp, t, (1337 << 32) | t, scale=res, rounding=rounding)
         if ev is not None:
             ev[1].record(stream)
 
@@ -233,9 +264,11 @@ def main():
     norm_ms = [s0.elapsed_time(a) for a, _, s0 in evs]
     step_ev_ms = sorted(s0.elapsed_time(z) for _, z, s0 in evs)
     gparams = S / (ms_step * 1e-3) / 1e9
-    step_gbs = (UPDATE_BYTES + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
-    achieved = UPDATE_BYTES * S / (upd_avg * 1e-3) / 1e9
-    traffic = measured_traffic(w.name) if (args.layout == "flat" and not args.pad) else None
+    step_gbs = (upd_bytes + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
+    achieved = upd_bytes * S / (upd_avg * 1e-3) / 1e9
+    default_variant = args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
+    traffic = measured_traffic(w.name) if default_variant else None
+    last_seed = (1337 << 32) | (args.warmup + 2 * args.steps)
     sumsq, norm, scale = bfo.read_norm_result(res)
 
     out = {
@@ -254,13 +287,14 @@ def main():
         "config": {"workload": w.name + (f"+pad{args.pad}" if args.pad else ""), "n_total": w.n,
                    "layout": args.layout, "shard": [b, e], "shard_elems": S,
                    "world": w.world, "rank": w.rank, "tensors": len(w.tensors),
-                   "grad_pool": len(pool), "bytes_per_param_step": UPDATE_BYTES + NORM_BYTES},
+                   "grad_pool": len(pool), "bytes_per_param_step": upd_bytes + NORM_BYTES,
+                   "update": variant},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "adamwTileKernel<master,SR>",
+        "roofline": {"bound": "hbm", "kernel": f"adamwTileKernel<{variant}>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": UPDATE_BYTES * S,
+                     "algorithmic_bytes_per_launch": upd_bytes * S,
                      "update_ms_avg": round(upd_avg, 5)},
         "step_ms_events": {"mean": round(sum(step_ev_ms) / len(step_ev_ms), 5),
                            "median": round(statistics.median(step_ev_ms), 5),
@@ -276,10 +310,12 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
         del src, dst
+    if M is not None:
+        out["rebuild"] = rebuild_rate(torch, bfo, stream, T, M, P, last_seed, args.steps)
     if not args.no_cpu_baseline and args.layout == "flat":
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
-        out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds)
-    if not args.no_ceiling:
+        out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds, args.rounding == "sr")
+    if not args.no_ceiling and M is not None:
         out["ceiling"] = stream_ceiling(torch, bfo, stream, P[:S], pool[0][:S], M, m, v, args.steps, achieved)
     print(json.dumps(out), flush=True)
 
