@@ -108,6 +108,39 @@ def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
             "single_thread_value": one}
 
 
+def checkpoint_rate(torch, bfo, T, P, M, m, v, seed, directory):
+    """Save this rank's optimizer state, mark it done, find it as the latest,
+    load it into fresh buffers and check every byte; time save and load."""
+    import shutil
+
+    step_no = 1
+    os.makedirs(directory, exist_ok=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    bfo.checkpoint_save(directory, T, m, v, step_no, seed, master=M, params=None if M is not None else P)
+    bfo.checkpoint_done(directory, step_no)
+    t_save = time.perf_counter() - t0
+    assert bfo.checkpoint_latest(directory) == step_no
+    m2, v2 = torch.empty_like(m), torch.empty_like(v)
+    M2 = torch.empty_like(M) if M is not None else None
+    P2 = torch.empty_like(P) if M is None else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    got_seed = bfo.checkpoint_load(directory, step_no, T, m2, v2, master=M2, params=P2)
+    torch.cuda.synchronize()
+    t_load = time.perf_counter() - t0
+    same = got_seed == seed and all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+                                   for a, b in ((m, m2), (v, v2)) + (((M, M2),) if M is not None else ()))
+    if M is None:
+        same = same and torch.equal(P.view(torch.int16), P2.view(torch.int16))
+    nbytes = sum(os.path.getsize(os.path.join(directory, f)) for f in os.listdir(directory))
+    shutil.rmtree(directory, ignore_errors=True)
+    del m2, v2, M2, P2
+    return {"bytes": nbytes, "save_s": round(t_save, 3), "load_s": round(t_load, 3),
+            "save_GBps": round(nbytes / t_save / 1e9, 2), "load_GBps": round(nbytes / t_load / 1e9, 2),
+            "round_trip_bit_exact": bool(same), "dir": directory}
+
+
 def rebuild_rate(torch, bfo, stream, T, M, P, seed, launches):
     """master_to_bf16_sr (the resume-time rebuild, 6 B per parameter) timed per
     launch with HIP events on the launch stream.  It rewrites P from the
@@ -163,6 +196,12 @@ def main():
                     help="time the no-master update (old weights read from the bf16 params, 22 B/param)")
     ap.add_argument("--rounding", choices=("sr", "rne"), default="sr",
                     help="bf16 write-back: stochastic (default) or round to nearest even")
+    ap.add_argument("--step-control", action="store_true",
+                    help="per-step learning rate from a cosine schedule (host) and the device outlier "
+                         "detector (window 128, z > 6 skips) between the norm and the update")
+    ap.add_argument("--checkpoint-dir", default=None,
+                    help="after timing, save this rank's state there, load it back, check it bit for bit, "
+                         "time both and delete the files")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -222,15 +261,34 @@ def main():
     rounding = bfo.ROUND_RNE if args.rounding == "rne" else bfo.ROUND_SR
     upd_bytes = UPDATE_BYTES_NO_MASTER if args.no_master else UPDATE_BYTES
     variant = ("no-master" if args.no_master else "master") + "," + args.rounding.upper()
+    last_t = args.warmup + 2 * args.steps
+    outlier, hps = None, None
+    if args.step_control:
+        # Cosine schedule over every step this run makes; the detector's window
+        # is filled beforehand with the norms of the gradient pool in the order
+        # the steps use them, so that the timed steps pay for the full z-score
+        # pass (an identical value throughout would give a zero variance).
+        hps = [None] + [bfo.AdamwHParams(bfo.lr_at(bfo.LR_COSINE, t - 1, 10, last_t, w.hparams.lr, 0.1),
+                                         w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
+                                         w.hparams.weight_decay, 1) for t in range(1, last_t + 1)]
+        outlier = bfo.Outlier(window=128, threshold=6.0, device=dev)
+        for k in range(128):
+            bfo.grad_global_norm(T, pool[k % len(pool)], res, w.hparams.max_norm)
+            outlier.update(bfo.norm_ptr(res))
+    skips = torch.zeros(1, dtype=torch.int64, device=dev)
 
     def step(t, ev=None):
         G = pool[(t - 1) % len(pool)]
         if ev is not None:
             ev[2].record(stream)
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
+        skip = None
+        if outlier is not None:
+            skip = outlier.update(bfo.norm_ptr(res)).skip
         if ev is not None:
             ev[0].record(stream)
-        bfo.adamw_sr_step(T, P, G, M, m, v, hp, t, (1337 << 32) | t, scale=res, rounding=rounding)
+        bfo.adamw_sr_step(T, P, G, M, m, v, hps[t] if hps else hp, t, (1337 << 32) | t, scale=res,
+                          rounding=rounding, skip=skip)
         if ev is not None:
             ev[1].record(stream)
 
@@ -259,6 +317,13 @@ def main():
     for k in range(args.steps):
         step(args.warmup + args.steps + 1 + k, evs[k])
     torch.cuda.synchronize()
+    if outlier is not None:
+        # Evidence that no timed step was skipped: the event-bracketed pass
+        # uses the same grads in the same order, so count its skips.
+        for k in range(args.steps):
+            step(args.warmup + args.steps + 1 + k)
+            skips.add_(outlier.skip)
+        torch.cuda.synchronize()
     upd_ms = [a.elapsed_time(z) for a, z, _ in evs]
     upd_avg = sum(upd_ms) / len(upd_ms)
     norm_ms = [s0.elapsed_time(a) for a, _, s0 in evs]
@@ -268,7 +333,7 @@ def main():
     achieved = upd_bytes * S / (upd_avg * 1e-3) / 1e9
     default_variant = args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
     traffic = measured_traffic(w.name) if default_variant else None
-    last_seed = (1337 << 32) | (args.warmup + 2 * args.steps)
+    last_seed = (1337 << 32) | last_t      # seed of the last update (the check pass repeats the same t)
     sumsq, norm, scale = bfo.read_norm_result(res)
 
     out = {
@@ -302,6 +367,12 @@ def main():
                            "norm_mean": round(sum(norm_ms) / len(norm_ms), 5)},
         "last_norm": {"norm": norm, "scale": scale},
     }
+    if outlier is not None:
+        out["step_control"] = {"lr": "cosine, 10 warm-up steps, floor 0.1", "outlier_window": 128,
+                               "z_threshold": 6.0, "last_z": float(outlier.z.item()),
+                               "skipped_in_check_pass": int(skips.item())}
+    if args.checkpoint_dir:
+        out["checkpoint"] = checkpoint_rate(torch, bfo, T, P, M, m, v, last_seed, args.checkpoint_dir)
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

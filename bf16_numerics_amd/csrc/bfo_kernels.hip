@@ -610,41 +610,69 @@ __global__ __launch_bounds__(kBlock) void decayDumpKernel(ShardView sv, uint64_t
 constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 22;
 
 // ---------------------------------------------------------------------------
-// Outlier z-score ("04 · 多 GPU 与混合精度" §4): one lane compares the new
-// value with the window of previous finite values (binary64 mean and
-// population variance, summed oldest to newest), writes z (NaN until the
-// window is full) and the skip flag, then appends the value if finite.
+// Outlier z-score ("04 · 多 GPU 与混合精度" §4): compares the new value with
+// the window of previous finite values (binary64 mean and population
+// variance, each summed oldest to newest), writes z (NaN until the window is
+// full) and the skip flag, then appends the value if finite.  The wave copies
+// the ring into LDS in age order; one lane then runs the two serial sums in
+// that order, reading eight values per step.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ double sumOldestFirst(const float *win, uint32_t W, double mean, bool centered) {
+    double acc = 0.0;
+    uint32_t k = 0;
+    for (; k + 8 <= W; k += 8) {
+        const float4 a = *reinterpret_cast<const float4 *>(win + k);
+        const float4 b = *reinterpret_cast<const float4 *>(win + k + 4);
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (centered) {
+                const double d = double(x[e]) - mean;
+                acc += d * d;
+            } else {
+                acc += double(x[e]);
+            }
+        }
+    }
+    for (; k < W; ++k) {
+        if (centered) {
+            const double d = double(win[k]) - mean;
+            acc += d * d;
+        } else {
+            acc += double(win[k]);
+        }
+    }
+    return acc;
+}
+
 __global__ __launch_bounds__(64) void outlierUpdateKernel(OutlierState *st, const float *value, float threshold,
                                                           float *zOut, int32_t *skipOut) {
+    __shared__ __align__(16) float win[kOutlierMaxWindow];
+    const uint32_t W = st->window, count = st->count, head = st->head;
+    const bool full = count == W;
+    if (full) {
+        for (uint32_t k = threadIdx.x; k < W; k += 64) {
+            uint32_t idx = head + k;
+            if (idx >= W) idx -= W;
+            win[k] = st->values[idx];
+        }
+    }
+    __syncthreads();
     if (threadIdx.x != 0) return;
     const float x = *value;
-    const uint32_t W = st->window;
     double z = __builtin_nan("");
-    if (st->count == W) {
-        double sum = 0.0;
-        for (uint32_t k = 0; k < W; ++k) {
-            uint32_t idx = st->head + k;
-            if (idx >= W) idx -= W;
-            sum += double(st->values[idx]);
-        }
-        const double mean = sum / double(W);
-        double sq = 0.0;
-        for (uint32_t k = 0; k < W; ++k) {
-            uint32_t idx = st->head + k;
-            if (idx >= W) idx -= W;
-            const double dev = double(st->values[idx]) - mean;
-            sq += dev * dev;
-        }
+    if (full) {
+        const double mean = sumOldestFirst(win, W, 0.0, false) / double(W);
+        const double sq = sumOldestFirst(win, W, mean, true);
         z = (double(x) - mean) / sqrt(sq / double(W));
     }
     const bool finite = (__float_as_uint(x) & 0x7F800000u) != 0x7F800000u;
     *zOut = float(z);
     *skipOut = (!finite || (threshold > 0.0f && z > double(threshold))) ? 1 : 0;
     if (finite) {
-        st->values[st->head] = x;
-        st->head = st->head + 1 == W ? 0u : st->head + 1;
-        if (st->count < W) st->count = st->count + 1;
+        st->values[head] = x;
+        st->head = head + 1 == W ? 0u : head + 1;
+        if (count < W) st->count = count + 1;
     }
 }
 
