@@ -27,6 +27,7 @@ UPDATE_BYTES_NO_MASTER = 22    # G 2 + P 2+2 + m 4+4 + v 4+4
 NORM_BYTES = 2                 # G read once
 REBUILD_BYTES = 6              # master_to_bf16_sr: M 4 read + P 2 written
 METRIC = "optimizer Gparams/s per step + achieved HBM GB/s (% of peak), 1 MI355X"
+WORKLOAD_NAMES = ("tiny_gpt_d32", "gpt2_124m", "gpt2_1p5b_shard", "stall16m", "llama7b")
 
 
 def kernel_source_digest():
@@ -186,7 +187,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2_1p5b_shard")
+    ap.add_argument("--workload", default="gpt2_1p5b_shard",
+                    choices=WORKLOAD_NAMES)
     ap.add_argument("--grad-pool", type=int, default=4)
     ap.add_argument("--layout", choices=("flat", "per_tensor"), default="flat",
                     help="ZeRO-1 shard layout: contiguous range, or 1/N of every tensor")
@@ -261,7 +263,7 @@ def main():
     rounding = bfo.ROUND_RNE if args.rounding == "rne" else bfo.ROUND_SR
     upd_bytes = UPDATE_BYTES_NO_MASTER if args.no_master else UPDATE_BYTES
     variant = ("no-master" if args.no_master else "master") + "," + args.rounding.upper()
-    last_t = args.warmup + 2 * args.steps
+    last_t = args.warmup + 2 * args.steps + 1   # warm-up, timed, lead, event-bracketed steps
     outlier, hps = None, None
     if args.step_control:
         # Cosine schedule over every step this run makes; the detector's window
@@ -313,19 +315,28 @@ def main():
     # Per-launch duration of the dominant kernel (the update): K more steps with
     # HIP events recorded on the launch stream around each update call.  Kept
     # out of the region above because each event adds a few microseconds of gap.
+    # The events are created (first record) beforehand and an untimed step
+    # leads the pass, so the host is ahead of the GPU from the first interval
+    # on and no host delay can fall inside one.
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    for tpl in evs:
+        for ev_k in tpl:
+            ev_k.record(stream)
+    t_lead = args.warmup + args.steps + 1
+    step(t_lead)
     for k in range(args.steps):
-        step(args.warmup + args.steps + 1 + k, evs[k])
+        step(t_lead + 1 + k, evs[k])
     torch.cuda.synchronize()
     if outlier is not None:
         # Evidence that no timed step was skipped: the event-bracketed pass
         # uses the same grads in the same order, so count its skips.
         for k in range(args.steps):
-            step(args.warmup + args.steps + 1 + k)
+            step(t_lead + 1 + k)
             skips.add_(outlier.skip)
         torch.cuda.synchronize()
     upd_ms = [a.elapsed_time(z) for a, z, _ in evs]
     upd_avg = sum(upd_ms) / len(upd_ms)
+    upd_median = statistics.median(upd_ms)
     norm_ms = [s0.elapsed_time(a) for a, _, s0 in evs]
     step_ev_ms = sorted(s0.elapsed_time(z) for _, z, s0 in evs)
     gparams = S / (ms_step * 1e-3) / 1e9
@@ -360,7 +371,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": upd_bytes * S,
-                     "update_ms_avg": round(upd_avg, 5)},
+                     "update_ms_avg": round(upd_avg, 5), "update_ms_median": round(upd_median, 5)},
         "step_ms_events": {"mean": round(sum(step_ev_ms) / len(step_ev_ms), 5),
                            "median": round(statistics.median(step_ev_ms), 5),
                            "min": round(step_ev_ms[0], 5), "max": round(step_ev_ms[-1], 5),

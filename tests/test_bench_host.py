@@ -17,6 +17,10 @@ import bench  # noqa: E402
 from bf16_numerics_amd import workloads as W  # noqa: E402
 
 
+def test_workload_choices_match_the_generators():
+    assert set(bench.WORKLOAD_NAMES) == set(W.WORKLOADS)
+
+
 def test_more_than_one_gpu_is_refused_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
