@@ -40,8 +40,11 @@
  *     every buffer; the library keeps no pointer after a call returns.
  *   - Asynchrony.  GPU work is queued on `stream` (a hipStream_t; NULL means
  *     the null stream) and the call returns without waiting for it.  Argument
- *     errors are reported synchronously and queue no work.  Nothing here
- *     synchronises the host or allocates memory per call.
+ *     errors are reported synchronously and queue no work.  Apart from the
+ *     checkpoint calls (which move state through files, and so wait for their
+ *     copies and use a pinned host stage for the call's length), nothing here
+ *     synchronises the host or allocates memory per call; device memory is
+ *     allocated only when a table or an outlier detector is created.
  *   - Errors.  Every function returns BFO_OK (0) or a negative BFO_E* code;
  *     bfo_status_string() names it.  BFO_EHIP means a HIP runtime call
  *     failed; bfo_last_hip_error() gives its hipError_t code for the calling
@@ -49,6 +52,16 @@
  *   - Concurrency.  A table may be used from several threads, but calls on
  *     one table whose GPU work overlaps in time (different streams without
  *     ordering) race on the table's norm workspace.
+ *
+ * A step, as a ZeRO-1 rank runs it (error checks left out):
+ *   bfo_table tb;  bfo_table_create(tensors, count, world, rank, &tb);   once
+ *   bfo_norm_result *res;  (16-byte aligned device memory)              once
+ *   per step t = 1, 2, ...:
+ *     grad_global_norm(tb, grads + begin, 1.0f, res, stream);
+ *     adamw_sr_step(tb, params + begin, grads + begin, master, m, v, &hp,
+ *                   &res->scale, NULL, t, seed_t, BFO_ROUND_SR, stream);
+ *   (the all-gather of params and the reduce-scatter of grads around it are
+ *   the caller's; every array here is already resident on the device.)
  */
 #ifndef BF16OPT_H
 #define BF16OPT_H
