@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--grad-pool", type=int, default=4)
     ap.add_argument("--layout", choices=("flat", "per_tensor"), default="flat",
                     help="ZeRO-1 shard layout: contiguous range, or 1/N of every tensor")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="ZeRO-1 rank whose shard is timed (default: the workload's own, rank 1 of 8 for the "
+                         "1.5B shard)")
     ap.add_argument("--pad", type=int, default=0,
                     help="append a 1-D tensor of this many elements (e.g. 8 makes n/8 odd: misaligned shards)")
     ap.add_argument("--no-master", action="store_true",
@@ -226,6 +229,10 @@ def main():
     w = W.WORKLOADS[args.workload]()
     if args.pad:
         w.tensors = list(w.tensors) + [("pad", (args.pad,))]
+    if args.rank is not None:
+        if not 0 <= args.rank < w.world:
+            ap.error(f"--rank must be in [0, {w.world}) for {w.name}")
+        w.rank = args.rank
     layout = bfo.LAYOUT_PER_TENSOR if args.layout == "per_tensor" else bfo.LAYOUT_FLAT
     T = bfo.Table(w.entries(), w.world, w.rank, layout=layout)
     S = T.size
@@ -342,7 +349,8 @@ def main():
     gparams = S / (ms_step * 1e-3) / 1e9
     step_gbs = (upd_bytes + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
     achieved = upd_bytes * S / (upd_avg * 1e-3) / 1e9
-    default_variant = args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
+    default_variant = (args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
+                       and args.rank is None)
     traffic = measured_traffic(w.name) if default_variant else None
     last_seed = (1337 << 32) | last_t      # seed of the last update (the check pass repeats the same t)
     sumsq, norm, scale = bfo.read_norm_result(res)
