@@ -431,7 +431,7 @@ def full_size_step(bfo, w, rank, steps=1):
 
 def test_full_size_gpt2_1p5b_shard(bfo):
     w = W.gpt2_1p5b_shard()
-    for rank in (1, 0, 7):
+    for rank in (1, 0, 2, 3, 4, 5, 6, 7):
         got = full_size_step(bfo, w, rank, steps=2 if rank == 1 else 1)
         print(f"gpt2_1p5b rank {rank}: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
 
@@ -441,6 +441,42 @@ def test_full_size_llama7b(bfo):
     got = full_size_step(bfo, w, 0, steps=2)
     print(f"llama7b: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
     assert got[2] < 1.0
+
+
+def test_full_size_gpt2_1p5b_eight_shards_equal_the_unsharded_step(bfo):
+    # The ZeRO-1 invariant at full size: the 8 ranks' flat shards, stepped
+    # with the global clip scale into one shared param buffer, reproduce the
+    # unsharded two-step run bit for bit (P, M, m, v), and the 8 per-rank
+    # sums of squares add up to the global one.
+    w = W.gpt2_1p5b_shard()
+    ents = w.entries()
+    n = w.n
+    P0, M0, _, _ = W.init_state(torch, w, 0, n, DEV)
+    G = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    Tfull = bfo.Table(ents)
+    res = bfo.new_norm_result(DEV)
+    ref = {"P": P0.clone(), "M": M0.clone(), "m": torch.zeros(n, device=DEV), "v": torch.zeros(n, device=DEV)}
+    sh = {"P": P0, "M": M0, "m": torch.zeros(n, device=DEV), "v": torch.zeros(n, device=DEV)}
+    tables = [bfo.Table(ents, w.world, r) for r in range(w.world)]
+    rres = bfo.new_norm_result(DEV)
+    for t in (1, 2):
+        W.fill_grads(torch, w, G, 0, t)
+        bfo.grad_global_norm(Tfull, G, res, w.hparams.max_norm)
+        bfo.adamw_sr_step(Tfull, ref["P"], G, ref["M"], ref["m"], ref["v"], w.hparams, t, step_seed(t), scale=res)
+        total = 0.0
+        for T in tables:
+            b, e = T.begin, T.end
+            bfo.grad_global_norm(T, G[b:e], rres, w.hparams.max_norm)
+            total += bfo.read_norm_result(rres)[0]
+            bfo.adamw_sr_step(T, sh["P"][b:e], G[b:e], sh["M"][b:e], sh["m"][b:e], sh["v"][b:e], w.hparams, t,
+                              step_seed(t), scale=res)
+        glob = bfo.read_norm_result(res)[0]
+        assert abs(total - glob) <= 1e-12 * glob, (total, glob)
+        for k in ("P", "M", "m", "v"):
+            a = sh[k].view(torch.int16 if k == "P" else torch.int32)
+            r = ref[k].view(torch.int16 if k == "P" else torch.int32)
+            assert torch.equal(a, r), f"{k} differs from the unsharded run at t={t}"
+        print(f"t={t}: 8 shards == unsharded (n={n}), sumsq {glob:.6f}", flush=True)
 
 
 def test_full_size_gpt2_1p5b_per_tensor(bfo):
