@@ -259,7 +259,8 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo
     if (!alignedTo(grads, 2) || !alignedTo(out, 16)) return BFO_EMISALIGNED;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
-    hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0, max_norm,
+    hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0,
+                                    table->layout == BFO_LAYOUT_FLAT, max_norm,
                                     table->normPartials, out, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }

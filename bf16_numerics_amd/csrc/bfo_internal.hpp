@@ -74,7 +74,7 @@ TableFacts tableFacts(const bfo_table_s *table);
 // through the runs and are at least 2-byte aligned; pgVec says whether P
 // and G are 16-byte aligned (then 8-element vectors at 8-aligned positions
 // use 16-byte accesses).
-hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, float maxNorm,
+hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, bool flat, float maxNorm,
                       double *partials, bfo_norm_result *out, hipStream_t stream);
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
                        ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,

@@ -537,6 +537,39 @@ __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__res
     if (threadIdx.x == 0) partials[tile] = total;
 }
 
+// Flat shards with 16-byte-aligned grads: shard element j is grads[j], so a
+// lane's address needs no plan lookup (two dependent loads that would stand
+// before every grad load and cost a quarter of the bandwidth).  Same tiles,
+// lane-to-vector map, order of additions and partial slots as
+// normStage1Kernel, hence the same bits.
+__global__ __launch_bounds__(kBlock) void normStage1FlatKernel(const uint16_t *__restrict__ G, uint64_t S,
+                                                               double *__restrict__ partials, uint64_t tileBase,
+                                                               uint64_t lastTile) {
+    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
+    const uint64_t full = S / 8;  // vectors with all eight elements in the shard
+    uint4 x[kNormVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kNormVecPerLane; ++k) {
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (q < full) x[k] = reinterpret_cast<const uint4 *>(G)[q];
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kNormVecPerLane; ++k) {
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (q < full) {
+            acc = sumSquares8(acc, x[k]);
+        } else if (q * 8 < S) {
+            for (uint64_t j = q * 8; j < S; ++j) {
+                const double d = double(bf16At(G, j));
+                acc = __builtin_fma(d, d, acc);
+            }
+        }
+    }
+    const double total = blockSum<kBlock>(acc);
+    if (threadIdx.x == 0) partials[tile] = total;
+}
+
 __global__ __launch_bounds__(kBlock) void normReduceKernel(const double *__restrict__ in, uint64_t count,
                                                            double *__restrict__ out) {
     const uint64_t lo = uint64_t(blockIdx.x) * kNormReduceRun;
@@ -700,13 +733,17 @@ hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, floa
 
 }  // namespace
 
-hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, float maxNorm,
+hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, bool flat, float maxNorm,
                       double *partials, bfo_norm_result *out, hipStream_t stream) {
     const uint64_t ntiles = normTiles(S);
     for (uint64_t base = 0; base < ntiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = ntiles - base < kMaxBlocksPerLaunch ? ntiles - base : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, S, sv, pgVec,
-                           partials, base, ntiles - 1);
+        if (flat && pgVec)
+            hipLaunchKernelGGL(normStage1FlatKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, S, partials,
+                               base, ntiles - 1);
+        else
+            hipLaunchKernelGGL(normStage1Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, g, S, sv, pgVec,
+                               partials, base, ntiles - 1);
     }
     const double *finishIn = partials;
     uint64_t finishCount = ntiles;

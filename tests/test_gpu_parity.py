@@ -150,6 +150,30 @@ def test_norm_sizes(bfo, n):
         assert got == (0.0, 0.0, 1.0)
 
 
+@pytest.mark.parametrize("make", [W.tiny, lambda: ragged_workload(9, 13), W.gpt2_124m])
+def test_norm_flat_fast_path_equals_plan_path_bit_for_bit(bfo, make):
+    # A flat table with 16-byte-aligned grads reads them directly; a
+    # per-tensor table of one rank and a flat table given a 2-byte-aligned
+    # copy go through the shard plan.  Same elements in the same order, same
+    # partition: the three results must agree in every bit.
+    w = make()
+    ents = w.entries()
+    G = torch.empty(w.n, dtype=torch.bfloat16, device=DEV)
+    W.fill_grads(torch, w, G, 0, 1)
+    buf = torch.zeros(w.n + 8, dtype=torch.bfloat16, device=DEV)
+    buf[1:1 + w.n] = G
+    Gmis = buf[1:1 + w.n]
+    assert Gmis.data_ptr() % 16 != 0
+    got = []
+    for T, g in ((bfo.Table(ents), G), (bfo.Table(ents, 1, 0, layout=bfo.LAYOUT_PER_TENSOR), G),
+                 (bfo.Table(ents), Gmis)):
+        res = bfo.new_norm_result(DEV)
+        bfo.grad_global_norm(T, g, res, w.hparams.max_norm)
+        got.append(res.cpu().numpy().tobytes())
+    assert got[0] == got[1] == got[2]
+    assert_norm_parity(bfo.read_norm_result(res), o.grad_norm(u16(G), w.hparams.max_norm))
+
+
 def test_norm_closed_form_and_extremes(bfo):
     assert _norm_case(bfo, np.full(1 << 24, 0x3A80, np.uint16)) == (16.0, 4.0, 0.25)
     assert _norm_case(bfo, np.zeros(1000, np.uint16)) == (0.0, 0.0, 1.0)
