@@ -12,7 +12,7 @@
  *           chapter: §2.1 precision roles, §2.2 the AdamW kernel, §2.3
  *           stochastic rounding, §3.2 ZeRO-1 sharding rule, §4 the training
  *           step (grad norm and clip), §5.2 bit-perfect resume.
- *   [L13]   "第 13 讲：扩大 LLM——优化与并行训练" -- §1.4 Adam, §1.7 bias
+ *   [LEC13] "第 13 讲：扩大 LLM——优化与并行训练" -- §1.4 Adam, §1.7 bias
  *           correction and AdamW, §2.1 number formats, §2.3 fp32 master
  *           weights, §5.2 ZeRO-1, §7.3 exercises 1 and 5.
  *   [DIST]  "LLM 分布式训练实战：CUDA/ROCm 多卡并行优化详解" -- §3.1 the
@@ -65,7 +65,7 @@ typedef struct {
 static uint32_t f32_bits(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
 static float bits_f32(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
 
-/* [L13] §2.1: bf16 keeps fp32's sign and 8 exponent bits and the top 7
+/* [LEC13] §2.1: bf16 keeps fp32's sign and 8 exponent bits and the top 7
  * mantissa bits, i.e. it is the upper half of a binary32 pattern.  Widening
  * is therefore exact: the pattern goes to the upper 16 bits. */
 float oracle_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
@@ -80,7 +80,7 @@ static double bf16_value_for_rounding(uint16_t h) {
 }
 
 /* Round-to-nearest, ties to even ([LLMC] §2.3 "ordinary rounding to the
- * nearest bf16"; [L13] §7.3 exercise 5: 1 + 2^-8 lies exactly half way and
+ * nearest bf16"; [LEC13] §7.3 exercise 5: 1 + 2^-8 lies exactly half way and
  * goes to the even neighbour 1, 257 goes to 256).  Written as the
  * definition: of the two bf16 values that bracket x, return the nearer one
  * and, on a tie, the one whose last mantissa bit is 0.  NaN stays a quiet
@@ -263,7 +263,7 @@ void oracle_grad_norm(const uint16_t *g, uint64_t count, float max_norm,
 /* AdamW step                                                           */
 /* ------------------------------------------------------------------ */
 
-/* [L13] §1.7: m and v start at 0, so without correction the step is scaled
+/* [LEC13] §1.7: m and v start at 0, so without correction the step is scaled
  * by (1 - beta1^t) / sqrt(1 - beta2^t); dividing m by 1 - beta1^t and v by
  * 1 - beta2^t removes it.  beta^t is formed as pow() in binary64 and
  * 1 - beta^t is rounded once to binary32.  t is the 1-based step number
@@ -282,7 +282,7 @@ static float lerp2fma(float start, float end, float w) {
     return fmaf(w, end, fmaf(-w, start, start));
 }
 
-/* The AdamW step, per element ([LLMC] §2.2, with [L13] §1.7 for the bias
+/* The AdamW step, per element ([LLMC] §2.2, with [LEC13] §1.7 for the bias
  * correction and the decoupled weight decay):
  *   grad = grad_scale * f32(G)
  *   m    = lerp(grad, m, beta1)           v = lerp(grad*grad, v, beta2)
