@@ -41,8 +41,9 @@ struct bfo_table_s {
     uint64_t *rng = nullptr;         // [nruns]
     uint8_t *flag = nullptr;         // [nruns]
     double *normPartials = nullptr;  // [normTiles(S) + normRuns(...)], at least 1
+    uint64_t *normOffset = nullptr;  // [normTiles(S)], per-tensor tables only
 
-    bfo::ShardView view() const { return {tile, local, addr, rng, flag}; }
+    bfo::ShardView view() const { return {tile, local, addr, rng, flag, normOffset}; }
 };
 
 bfo::TableFacts bfo::tableFacts(const bfo_table_s *t) {
@@ -140,6 +141,25 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
         tileWord[t] = uint32_t(k) | (local[k + 1] < t1 ? bfo::kTileMixed : 0u);
     }
 
+    // Per-tensor tables: grad-norm tiles that lie inside one run are read at a
+    // constant offset from the shard-local position (8-aligned, so a
+    // 16-byte-aligned grads array keeps 16-byte vectors).
+    std::vector<uint64_t> normOff;
+    if (layout == BFO_LAYOUT_PER_TENSOR && S > 0) {
+        const uint64_t tileElems = bfo::kNormTileVecs * 8;
+        const uint64_t nT = bfo::normTiles(S);
+        normOff.assign(nT, bfo::kNoNormOffset);
+        uint64_t r = 0;
+        for (uint64_t t = 0; t < nT; ++t) {
+            const uint64_t t0 = t * tileElems;
+            const uint64_t t1 = t0 + tileElems < S ? t0 + tileElems : S;
+            while (runs[r].local + runs[r].length <= t0) ++r;
+            const bfo_run &run = runs[r];
+            const uint64_t off = run.addr - run.local;
+            if (t1 <= run.local + run.length && off % 8 == 0) normOff[t] = off;
+        }
+    }
+
     // Fingerprint of the table, stored in checkpoints to refuse a mismatch.
     uint64_t fp = 1469598103934665603ull;
     auto mix = [&fp](uint64_t x) {
@@ -178,7 +198,8 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
     const uint64_t offRng = offAddr + up(addr.size() * sizeof(uint64_t));
     const uint64_t offFlag = offRng + up(rng.size() * sizeof(uint64_t));
     const uint64_t offNorm = offFlag + up(flag.size());
-    const uint64_t bytes = offNorm + up(nNorm * sizeof(double));
+    const uint64_t offNormOff = offNorm + up(nNorm * sizeof(double));
+    const uint64_t bytes = offNormOff + up(normOff.size() * sizeof(uint64_t));
     he = hipMalloc(&tb->devBlock, bytes);
     if (he != hipSuccess) {
         delete tb;
@@ -191,6 +212,7 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
     tb->rng = reinterpret_cast<uint64_t *>(base + offRng);
     tb->flag = reinterpret_cast<uint8_t *>(base + offFlag);
     tb->normPartials = reinterpret_cast<double *>(base + offNorm);
+    tb->normOffset = normOff.empty() ? nullptr : reinterpret_cast<uint64_t *>(base + offNormOff);
     if ((he = hipMemcpy(tb->tile, tileWord.data(), tileWord.size() * sizeof(uint32_t),
                         hipMemcpyHostToDevice)) != hipSuccess ||
         (he = hipMemcpy(tb->local, local.data(), local.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) !=
@@ -199,7 +221,9 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
             hipSuccess ||
         (he = hipMemcpy(tb->rng, rng.data(), rng.size() * sizeof(uint64_t), hipMemcpyHostToDevice)) !=
             hipSuccess ||
-        (he = hipMemcpy(tb->flag, flag.data(), flag.size(), hipMemcpyHostToDevice)) != hipSuccess) {
+        (he = hipMemcpy(tb->flag, flag.data(), flag.size(), hipMemcpyHostToDevice)) != hipSuccess ||
+        (!normOff.empty() && (he = hipMemcpy(tb->normOffset, normOff.data(), normOff.size() * sizeof(uint64_t),
+                                             hipMemcpyHostToDevice)) != hipSuccess)) {
         (void)hipFree(tb->devBlock);
         delete tb;
         return hipFail(he);

@@ -49,7 +49,13 @@ struct ShardView {
     const uint64_t *addr;
     const uint64_t *rng;
     const uint8_t *flag;
+    // Per-tensor tables: for each grad-norm tile, the constant (position in
+    // the grads array) - (shard element) when the whole tile lies in one run
+    // and that difference is a multiple of 8, else kNoNormOffset.  Null for
+    // flat tables (whose grads are shard-local anyway).
+    const uint64_t *normOffset;
 };
+constexpr uint64_t kNoNormOffset = UINT64_MAX;
 
 struct StepScalars {
     float lr, beta1, beta2, eps, wd, bc1, bc2;

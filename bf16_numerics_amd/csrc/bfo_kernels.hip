@@ -487,6 +487,44 @@ __device__ __forceinline__ double blockSum(double x) {
     return total;
 }
 
+// One tile of stage 1 when the tile's grads sit at consecutive positions
+// starting 16-byte aligned (shard element j at base[j]): a lane's address
+// needs no plan lookup (two dependent loads that would stand before every
+// grad load and cost a quarter of the bandwidth).  Same lane-to-vector map
+// and order of additions as the plan path, hence the same bits.
+__device__ __forceinline__ double normTileDirect(const uint16_t *__restrict__ base, uint64_t S, uint64_t tile) {
+    const uint64_t full = S / 8;  // vectors with all eight elements in the shard
+    uint4 x[kNormVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kNormVecPerLane; ++k) {
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (q < full) x[k] = reinterpret_cast<const uint4 *>(base)[q];
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kNormVecPerLane; ++k) {
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        if (q < full) {
+            acc = sumSquares8(acc, x[k]);
+        } else if (q * 8 < S) {
+            for (uint64_t j = q * 8; j < S; ++j) {
+                const double d = double(bf16At(base, j));
+                acc = __builtin_fma(d, d, acc);
+            }
+        }
+    }
+    return acc;
+}
+
+// Flat shards with 16-byte-aligned grads: shard element j is grads[j].
+__global__ __launch_bounds__(kBlock) void normStage1FlatKernel(const uint16_t *__restrict__ G, uint64_t S,
+                                                               double *__restrict__ partials, uint64_t tileBase,
+                                                               uint64_t lastTile) {
+    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
+    const double total = blockSum<kBlock>(normTileDirect(G, S, tile));
+    if (threadIdx.x == 0) partials[tile] = total;
+}
+
 // Workgroups take tiles from the shard's end backwards: the partial of a tile
 // depends only on its index, so the order changes no bit of the result, and the
 // lines read last (the shard's start) are the ones the update, which walks
@@ -496,6 +534,14 @@ __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__res
                                                            double *__restrict__ partials, uint64_t tileBase,
                                                            uint64_t lastTile) {
     const uint64_t tile = lastTile - (tileBase + blockIdx.x);
+    // A tile wholly inside one run whose grads start 16-byte aligned: element
+    // j sits at grads[j + offset] for one offset, so read it directly.
+    const uint64_t offset = (sv.normOffset && pgVec) ? sv.normOffset[tile] : kNoNormOffset;
+    if (offset != kNoNormOffset) {
+        const double total = blockSum<kBlock>(normTileDirect(G + offset, S, tile));
+        if (threadIdx.x == 0) partials[tile] = total;
+        return;
+    }
     uint4 x[kNormVecPerLane];
     Place pl[kNormVecPerLane];
     int mode[kNormVecPerLane];
@@ -529,39 +575,6 @@ __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__res
                 uint64_t addr, rng;
                 placeElement(sv, run, j, addr, rng);
                 const double d = double(bf16At(G, addr));
-                acc = __builtin_fma(d, d, acc);
-            }
-        }
-    }
-    const double total = blockSum<kBlock>(acc);
-    if (threadIdx.x == 0) partials[tile] = total;
-}
-
-// Flat shards with 16-byte-aligned grads: shard element j is grads[j], so a
-// lane's address needs no plan lookup (two dependent loads that would stand
-// before every grad load and cost a quarter of the bandwidth).  Same tiles,
-// lane-to-vector map, order of additions and partial slots as
-// normStage1Kernel, hence the same bits.
-__global__ __launch_bounds__(kBlock) void normStage1FlatKernel(const uint16_t *__restrict__ G, uint64_t S,
-                                                               double *__restrict__ partials, uint64_t tileBase,
-                                                               uint64_t lastTile) {
-    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
-    const uint64_t full = S / 8;  // vectors with all eight elements in the shard
-    uint4 x[kNormVecPerLane];
-#pragma unroll
-    for (int k = 0; k < kNormVecPerLane; ++k) {
-        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-        if (q < full) x[k] = reinterpret_cast<const uint4 *>(G)[q];
-    }
-    double acc = 0.0;
-#pragma unroll
-    for (int k = 0; k < kNormVecPerLane; ++k) {
-        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-        if (q < full) {
-            acc = sumSquares8(acc, x[k]);
-        } else if (q * 8 < S) {
-            for (uint64_t j = q * 8; j < S; ++j) {
-                const double d = double(bf16At(G, j));
                 acc = __builtin_fma(d, d, acc);
             }
         }

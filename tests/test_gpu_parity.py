@@ -172,6 +172,20 @@ def test_norm_flat_fast_path_equals_plan_path_bit_for_bit(bfo, make):
         got.append(res.cpu().numpy().tobytes())
     assert got[0] == got[1] == got[2]
     assert_norm_parity(bfo.read_norm_result(res), o.grad_norm(u16(G), w.hparams.max_norm))
+    # A per-tensor rank of four: tiles inside one run read at a fixed offset,
+    # the others through the plan; a 2-byte-aligned copy takes the plan for
+    # every tile.  Both must give the same bits, and the oracle's value.
+    if all(numel % 4 == 0 for _, numel, _ in ents):
+        T4 = bfo.Table(ents, 4, 1, layout=bfo.LAYOUT_PER_TENSOR)
+        pair = []
+        for g in (G, Gmis):
+            res = bfo.new_norm_result(DEV)
+            bfo.grad_global_norm(T4, g, res, w.hparams.max_norm)
+            pair.append(res.cpu().numpy().tobytes())
+        assert pair[0] == pair[1]
+        gidx = T4.global_index().astype(np.int64)
+        assert_norm_parity(bfo.read_norm_result(res), o.grad_norm(np.ascontiguousarray(u16(G)[gidx]),
+                                                                  w.hparams.max_norm))
 
 
 def test_norm_closed_form_and_extremes(bfo):
