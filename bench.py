@@ -163,10 +163,11 @@ def rebuild_rate(torch, bfo, stream, T, M, P, seed, launches):
 
 def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs):
     """Achievable bandwidth for the update's own traffic on this device: the
-    library's stream-mix kernel (same 14 B read + 14 B written per element in
-    the update's vector and workgroup plan, no arithmetic; key 0 leaves m, v
-    and the master unchanged and copies G into P), timed per launch with HIP
-    events on the launch stream, as the update is."""
+    library's stream-mix kernel (the update's bytes per element -- 14 read and
+    14 written with a master, 12 and 10 without -- in its vector and
+    workgroup plan, no arithmetic; key 0 leaves m, v and the master
+    unchanged), timed per launch with HIP events on the launch stream, as the
+    update is."""
     for _ in range(2):
         bfo.stream_mix(P, G, M, m, v, 0)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
@@ -176,7 +177,8 @@ def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs):
         z.record(stream)
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(z) for a, z in evs) / launches
-    gbs = UPDATE_BYTES * M.numel() / (ms * 1e-3) / 1e9
+    per = UPDATE_BYTES if M is not None else UPDATE_BYTES_NO_MASTER
+    gbs = per * m.numel() / (ms * 1e-3) / 1e9
     return {"kernel": "streamMixKernel (update traffic, no arithmetic)", "achieved": round(gbs, 1),
             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms, 5),
             "update_over_ceiling": round(update_gbs / gbs, 4)}
@@ -405,7 +407,7 @@ def main():
     if not args.no_cpu_baseline and args.layout == "flat":
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
         out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds, args.rounding == "sr")
-    if not args.no_ceiling and M is not None:
+    if not args.no_ceiling:
         out["ceiling"] = stream_ceiling(torch, bfo, stream, P[:S], pool[0][:S], M, m, v, args.steps, achieved)
     print(json.dumps(out), flush=True)
 

@@ -379,9 +379,10 @@ def decay_mask_dump(table):
 def stream_mix(params, grads, master, m, v, key=0):
     """The update's memory traffic without its arithmetic (bandwidth ceiling).
 
-    m, v, master ^= key as bit patterns; params = grads ^ (key & 0xFFFF)."""
-    count = master.numel()
-    dev = master.device
+    With a master: m, v, master ^= key as bit patterns and params = grads ^
+    (key & 0xFFFF).  master None: m, v ^= key and params ^= grads ^ (key & 0xFFFF)."""
+    count = m.numel()
+    dev = m.device
     args = [_arg(params, torch.bfloat16, count, "params", dev), _arg(grads, torch.bfloat16, count, "grads", dev),
             _arg(master, torch.float32, count, "master", dev), _arg(m, torch.float32, count, "m", dev),
             _arg(v, torch.float32, count, "v", dev)]

@@ -353,7 +353,7 @@ int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream) {
 int bfo_stream_mix(uint16_t *params, const uint16_t *grads, float *master, float *m, float *v, uint64_t count,
                    uint32_t key, void *stream) {
     if (count == 0) return BFO_OK;
-    if (!params || !grads || !master || !m || !v) return BFO_EINVAL;
+    if (!params || !grads || !m || !v) return BFO_EINVAL;
     if (!alignedTo(params, 16) || !alignedTo(grads, 16) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
         !alignedTo(v, 16))
         return BFO_EMISALIGNED;

@@ -326,17 +326,18 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
 // ---------------------------------------------------------------------------
 // Measurement kernel: the update's memory traffic without its arithmetic.
 // Same tile, lane and vector plan as the 16-byte path of adamwTileKernel
-// (reads G, m, v, M; writes m, v, M, P), with each output a bit-XOR of its
-// input and a key, so that nothing can be elided and key 0 leaves m, v, M
-// bitwise as they were and copies G into P.  Its bandwidth is the ceiling the
-// update can reach on a given device.
+// (with a master: reads G, m, v, M and writes m, v, M, P; without: reads G,
+// P, m, v and writes P, m, v), each output a bit-XOR of its inputs and a key,
+// so that nothing can be elided; key 0 leaves m, v and M bitwise as they
+// were.  Its bandwidth is the ceiling the update can reach on a given device.
 // ---------------------------------------------------------------------------
+template <bool kMaster>
 __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__ P, const uint16_t *__restrict__ G,
                                                           float *__restrict__ M, float *__restrict__ Mom,
                                                           float *__restrict__ Var, uint64_t count, uint32_t key,
                                                           uint64_t tileBase) {
     const uint64_t tile = tileBase + blockIdx.x;
-    uint4 gv[kVecPerLane], ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
+    uint4 gv[kVecPerLane], pv[kVecPerLane], ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
     uint4 wa[kVecPerLane], wb[kVecPerLane];
     int mode[kVecPerLane];
 #pragma unroll
@@ -349,8 +350,12 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
         mb[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q + 1];
         va[k] = reinterpret_cast<const uint4 *>(Var)[2 * q];
         vb[k] = reinterpret_cast<const uint4 *>(Var)[2 * q + 1];
-        wa[k] = reinterpret_cast<const uint4 *>(M)[2 * q];
-        wb[k] = reinterpret_cast<const uint4 *>(M)[2 * q + 1];
+        if constexpr (kMaster) {
+            wa[k] = reinterpret_cast<const uint4 *>(M)[2 * q];
+            wb[k] = reinterpret_cast<const uint4 *>(M)[2 * q + 1];
+        } else {
+            pv[k] = reinterpret_cast<const uint4 *>(P)[q];
+        }
     }
     const uint32_t key2 = (key & 0xFFFFu) | (key << 16);
 #pragma unroll
@@ -360,20 +365,29 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
             for (uint64_t j = q * 8; j < count; ++j) {
                 Mom[j] = __uint_as_float(__float_as_uint(Mom[j]) ^ key);
                 Var[j] = __uint_as_float(__float_as_uint(Var[j]) ^ key);
-                M[j] = __uint_as_float(__float_as_uint(M[j]) ^ key);
-                P[j] = uint16_t(G[j] ^ key);
+                if constexpr (kMaster) {
+                    M[j] = __uint_as_float(__float_as_uint(M[j]) ^ key);
+                    P[j] = uint16_t(G[j] ^ key);
+                } else {
+                    P[j] = uint16_t(P[j] ^ G[j] ^ key);
+                }
             }
             continue;
         }
         if (mode[k] != kRegular) continue;
         const uint4 kk = make_uint4(key, key, key, key);
+        const uint4 k2 = make_uint4(key2, key2, key2, key2);
         reinterpret_cast<uint4 *>(Mom)[2 * q] = ma[k] ^ kk;
         reinterpret_cast<uint4 *>(Mom)[2 * q + 1] = mb[k] ^ kk;
         reinterpret_cast<uint4 *>(Var)[2 * q] = va[k] ^ kk;
         reinterpret_cast<uint4 *>(Var)[2 * q + 1] = vb[k] ^ kk;
-        reinterpret_cast<uint4 *>(M)[2 * q] = wa[k] ^ kk;
-        reinterpret_cast<uint4 *>(M)[2 * q + 1] = wb[k] ^ kk;
-        reinterpret_cast<uint4 *>(P)[q] = gv[k] ^ make_uint4(key2, key2, key2, key2);
+        if constexpr (kMaster) {
+            reinterpret_cast<uint4 *>(M)[2 * q] = wa[k] ^ kk;
+            reinterpret_cast<uint4 *>(M)[2 * q + 1] = wb[k] ^ kk;
+            reinterpret_cast<uint4 *>(P)[q] = gv[k] ^ k2;
+        } else {
+            reinterpret_cast<uint4 *>(P)[q] = pv[k] ^ gv[k] ^ k2;
+        }
     }
 }
 
@@ -814,8 +828,12 @@ hipError_t launchStreamMix(uint16_t *P, const uint16_t *G, float *M, float *m, f
     const uint64_t tiles = (count + kTileElems - 1) / kTileElems;
     for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL(streamMixKernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m, v, count, key,
-                           base);
+        if (M)
+            hipLaunchKernelGGL(streamMixKernel<true>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m, v,
+                               count, key, base);
+        else
+            hipLaunchKernelGGL(streamMixKernel<false>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m, v,
+                               count, key, base);
     }
     return hipGetLastError();
 }

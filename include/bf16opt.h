@@ -239,11 +239,13 @@ int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
 /* Measurement export: the update's memory traffic with none of its
  * arithmetic, for an achievable-bandwidth ceiling measured the same way as
  * the update.  For j < count (device arrays of count elements):
- *   m[j], v[j], master[j] ^= key (as 32-bit patterns); params[j] = grads[j] ^
- *   (key & 0xFFFF).
- * Reads 14 and writes 14 bytes per element, in the update's 16-byte vector
- * and workgroup plan.  key 0 leaves m, v and master unchanged and copies
- * grads into params.  All five pointers 16-byte aligned (else
+ *   with a master: m[j], v[j], master[j] ^= key (as 32-bit patterns) and
+ *     params[j] = grads[j] ^ (key & 0xFFFF) -- 14 bytes read and 14 written
+ *     per element, as the master update;
+ *   master == NULL: m[j], v[j] ^= key and params[j] ^= grads[j] ^
+ *     (key & 0xFFFF) -- 12 read and 10 written, as the no-master update;
+ * in the update's 16-byte vector and workgroup plan.  key 0 leaves m, v and
+ * master unchanged.  Every non-null pointer 16-byte aligned (else
  * BFO_EMISALIGNED); count 0 is a no-op. */
 int bfo_stream_mix(uint16_t *params, const uint16_t *grads, float *master, float *m, float *v, uint64_t count,
                    uint32_t key, void *stream);
