@@ -236,7 +236,10 @@ def main():
             ap.error(f"--rank must be in [0, {w.world}) for {w.name}")
         w.rank = args.rank
     layout = bfo.LAYOUT_PER_TENSOR if args.layout == "per_tensor" else bfo.LAYOUT_FLAT
-    T = bfo.Table(w.entries(), w.world, w.rank, layout=layout)
+    bfo.Table(w.entries(), w.world, w.rank, layout=layout).close()     # first call pays library start-up
+    t0 = time.perf_counter()
+    T = bfo.Table(w.entries(), w.world, w.rank, layout=layout)      # host plan + one upload, once per table
+    table_ms = (time.perf_counter() - t0) * 1e3
     S = T.size
 
     if layout == bfo.LAYOUT_PER_TENSOR:
@@ -387,6 +390,7 @@ def main():
                            "min": round(step_ev_ms[0], 5), "max": round(step_ev_ms[-1], 5),
                            "norm_mean": round(sum(norm_ms) / len(norm_ms), 5)},
         "last_norm": {"norm": norm, "scale": scale},
+        "table_ms": round(table_ms, 3),
     }
     if outlier is not None:
         out["step_control"] = {"lr": "cosine, 10 warm-up steps, floor 0.1", "outlier_window": 128,
