@@ -366,6 +366,54 @@ def test_update_non_finite_grads(bfo):
     assert_state_parity(host_copy(st), h, "non-finite")
 
 
+def _special_state(n, master, seed=11):
+    """Finite state built from edge values: fp32 subnormals of both signs,
+    signed zeros, the smallest normal, values near the fp32 maximum, bf16
+    subnormal and near-boundary grads; no NaN (its payload is not pinned)."""
+    rs = np.random.default_rng(seed)
+    f = np.float32
+    m_vals = np.array([0.0, -0.0, 1e-40, -1e-40, 1.4e-45, -1.4e-45, 1.17549435e-38, -3.5e-39, 2.5e-3, -7.0e-4],
+                      f)
+    v_vals = np.array([0.0, 1e-40, 1.4e-45, 1.17549435e-38, 3.0e-39, 6.25e-6, 1e-12, 0.5], f)
+    w_vals = np.array([0.0, -0.0, 1e-40, -1e-40, 1.17549435e-38, 1.0, -1.0, 3.3e38, -3.3e38, 65504.0, 1e-3,
+                       -2.0 ** -126, 1.0 + 2.0 ** -9], f)
+    g_bits = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x5F0B, 0xDF0B,
+                       0x3A83, 0x2F80], np.uint16)     # 0x5F0B ~ 1e19: its square stays finite in fp32
+    pick = lambda vals: vals[rs.integers(0, vals.size, n)]
+    st = {"m": pick(m_vals), "v": pick(v_vals), "G": pick(g_bits)}
+    M = pick(w_vals)
+    st["M"] = M if master else None
+    st["P"] = (M.view(np.uint32) >> 16).astype(np.uint16) if master else pick(g_bits ^ np.uint16(0x0100))
+    return st
+
+
+@pytest.mark.parametrize("master", [True, False])
+@pytest.mark.parametrize("rounding", [o.ROUND_SR, o.ROUND_RNE])
+@pytest.mark.parametrize("bias_correction,t", [(True, 1), (True, 1000), (False, 7)])
+def test_update_edge_values_bit_exact(bfo, master, rounding, bias_correction, t):
+    # Subnormal moments and weights, signed zeros, near-overflow weights and
+    # bf16-subnormal grads go through the fp32 sequence with denormals kept:
+    # every output bit must equal the oracle's.
+    w = ragged_workload(3, 13, seed=9)
+    ents = w.entries()
+    T = bfo.Table(ents)
+    h = _special_state(w.n, master)
+    hp = W.HParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, bias_correction=bias_correction)
+    st = {"P": dev_bf16(h["P"], DEV), "G": dev_bf16(h["G"], DEV), "m": dev_f32(h["m"], DEV),
+          "v": dev_f32(h["v"], DEV), "M": dev_f32(h["M"], DEV) if master else None}
+    bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], hp, t, step_seed(t), scale=None,
+                      rounding=rounding)
+    ref = {k: (None if a is None else a.copy()) for k, a in h.items()}
+    o.adamw_step(o.table(ents), 0, ref["P"], ref["G"], ref["M"], ref["m"], ref["v"], oracle_hparams(hp), 1.0, t,
+                 step_seed(t), rounding)
+    got = host_copy(st)
+    assert np.array_equal(got["P"], ref["P"]), "bf16 params differ"
+    for k in ("m", "v") + (("M",) if master else ()):
+        assert np.array_equal(got[k].view(np.uint32), ref[k].view(np.uint32)), f"{k} differs"
+    sub = (np.abs(ref["m"]) < 1.17549435e-38) & (ref["m"] != 0)
+    assert sub.any(), "the case should leave subnormal moments"
+
+
 def test_empty_shard(bfo):
     T = bfo.Table([])
     res = bfo.new_norm_result(DEV)
