@@ -37,7 +37,7 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error", "bfo_lr_at",
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
            "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
-           "bfo_stream_mix")
+           "bfo_stream_mix", "bfo_plan_runs")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -111,6 +111,8 @@ def _lib():
         "bfo_rng_dump": (i32, [u64, u64, u64, vp, vp]),
         "bfo_decay_mask_dump": (i32, [vp, vp, vp]),
         "bfo_stream_mix": (i32, [vp, vp, vp, vp, vp, u64, u32, vp]),
+        "bfo_plan_runs": (i32, [ctypes.POINTER(BfoTensor), u32, u32, u32, i32, ctypes.POINTER(BfoRun), u32,
+                                ctypes.POINTER(u32), pu64]),
         "bfo_status_string": (ctypes.c_char_p, [i32]),
         "bfo_last_hip_error": (i32, []),
     }
@@ -162,6 +164,26 @@ def shard_range(n, world, rank):
     return b.value, e.value
 
 
+def _tensor_array(entries):
+    arr = (BfoTensor * max(1, len(entries)))()
+    for k, (off, numel, flags) in enumerate(entries):
+        arr[k].offset, arr[k].numel, arr[k].flags, arr[k].reserved = off, numel, flags, 0
+    return arr
+
+
+def plan_runs(entries, world=1, rank=0, layout=LAYOUT_FLAT):
+    """The shard plan on the host (no GPU): (status, S, [(local, addr, global, length, flags)])."""
+    arr = _tensor_array(entries)
+    cnt, S = ctypes.c_uint32(0), ctypes.c_uint64(0)
+    rc = _lib().bfo_plan_runs(arr, len(entries), world, rank, layout, None, 0, ctypes.byref(cnt), ctypes.byref(S))
+    if rc != OK:
+        return rc, 0, []
+    out = (BfoRun * max(1, cnt.value))()
+    rc = _lib().bfo_plan_runs(arr, len(entries), world, rank, layout, out, cnt.value, ctypes.byref(cnt),
+                              ctypes.byref(S))
+    return rc, S.value, [(r.local, r.addr, r.global_, r.length, r.flags) for r in out[:cnt.value]]
+
+
 def shard_range_status(n, world, rank):
     b, e = ctypes.c_uint64(0), ctypes.c_uint64(0)
     rc = _lib().shard_range(n, world, rank, ctypes.byref(b), ctypes.byref(e))
@@ -181,9 +203,7 @@ class Table:
     def __init__(self, entries, world=1, rank=0, device=None, layout=LAYOUT_FLAT):
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else
                                    torch.device(device).index or 0)
-        arr = (BfoTensor * max(1, len(entries)))()
-        for k, (off, numel, flags) in enumerate(entries):
-            arr[k].offset, arr[k].numel, arr[k].flags, arr[k].reserved = off, numel, flags, 0
+        arr = _tensor_array(entries)
         h = ctypes.c_void_p(None)
         with torch.cuda.device(self.device):
             _check("bfo_table_create_layout",

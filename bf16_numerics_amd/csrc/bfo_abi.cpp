@@ -63,15 +63,23 @@ int shard_range(uint64_t n, uint32_t world, uint32_t rank, uint64_t *begin, uint
     return BFO_OK;
 }
 
-int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
-                            int layout, bfo_table *out) {
-    if (!out || (count > 0 && !tensors)) return BFO_EINVAL;
-    *out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// The shard plan, on the host only: validates the table, then lists the runs
+// of the shard (see bfo_run).  Flat: each tensor's piece of [b, e), addressed
+// shard-locally.  Per tensor: rank r's 1/world slice of every tensor,
+// addressed in the full buffer.  Pieces that continue one another with the
+// same flag merge.  begin is b for flat tables and 0 for per-tensor ones.
+int buildPlan(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank, int layout,
+              std::vector<bfo_run> &runs, uint64_t &n, uint64_t &S, uint64_t &begin) {
+    if (count > 0 && !tensors) return BFO_EINVAL;
     if (layout != BFO_LAYOUT_FLAT && layout != BFO_LAYOUT_PER_TENSOR) return BFO_EINVAL;
     if (count >= bfo::kTileMixed) return BFO_ETABLE;  // run ids must fit in 31 bits
 
     // Table: contiguous from 0, known flag bits only, no overflow.
-    uint64_t n = 0;
+    n = 0;
     for (uint32_t k = 0; k < count; ++k) {
         if (tensors[k].offset != n || (tensors[k].flags & ~BFO_FLAG_DECAY) || tensors[k].reserved)
             return BFO_ETABLE;
@@ -82,10 +90,7 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
     int rc = shard_range(n, world, rank, &b, &e);
     if (rc != BFO_OK) return rc;
 
-    // Runs.  Flat: each tensor's piece of [b, e), addressed shard-locally.
-    // Per tensor: rank r's 1/world slice of every tensor, addressed in the
-    // full buffer.  Pieces that continue one another with the same flag merge.
-    std::vector<bfo_run> runs;
+    runs.clear();
     auto push = [&runs](uint64_t local, uint64_t addr, uint64_t global, uint64_t len, uint32_t flags) {
         if (!runs.empty()) {
             bfo_run &p = runs.back();
@@ -96,7 +101,7 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
         }
         runs.push_back(bfo_run{local, addr, global, len, flags, 0u});
     };
-    uint64_t S = 0;
+    S = 0;
     if (layout == BFO_LAYOUT_FLAT) {
         for (uint32_t k = 0; k < count; ++k) {
             const uint64_t lo = tensors[k].offset > b ? tensors[k].offset : b;
@@ -118,6 +123,38 @@ int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t 
         }
         b = 0;
     }
+    begin = b;
+    return BFO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bfo_plan_runs(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank, int layout,
+                  bfo_run *out, uint32_t capacity, uint32_t *nruns, uint64_t *shard_elems) {
+    if (!nruns) return BFO_EINVAL;
+    std::vector<bfo_run> runs;
+    uint64_t n = 0, S = 0, b = 0;
+    const int rc = buildPlan(tensors, count, world, rank, layout, runs, n, S, b);
+    if (rc != BFO_OK) return rc;
+    *nruns = uint32_t(runs.size());
+    if (shard_elems) *shard_elems = S;
+    if (out) {
+        if (capacity < runs.size()) return BFO_ERANGE;
+        std::memcpy(out, runs.data(), runs.size() * sizeof(bfo_run));
+    }
+    return BFO_OK;
+}
+
+int bfo_table_create_layout(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank,
+                            int layout, bfo_table *out) {
+    if (!out) return BFO_EINVAL;
+    *out = nullptr;
+    std::vector<bfo_run> runs;
+    uint64_t n = 0, S = 0, b = 0;
+    const int rc = buildPlan(tensors, count, world, rank, layout, runs, n, S, b);
+    if (rc != BFO_OK) return rc;
     const uint64_t nruns = runs.size();
     std::vector<uint64_t> local(nruns + 1), addr(nruns ? nruns : 1), rng(nruns ? nruns : 1);
     std::vector<uint8_t> flag(nruns ? nruns : 1, 0);

@@ -179,6 +179,14 @@ int bfo_table_info(bfo_table table, uint64_t *n, uint64_t *begin, uint64_t *end)
  * copies them (BFO_ERANGE if capacity < *count).  Host only. */
 int bfo_table_runs(bfo_table table, bfo_run *out, uint32_t capacity, uint32_t *count);
 
+/* The shard plan bfo_table_create_layout would build, computed on the host
+ * with no device and no table ("04 · 多 GPU 与混合精度" §3.2 for both layouts;
+ * "LLM 分布式训练实战" §3.1 for the flat offset): the same validation and
+ * status codes, *nruns = number of runs, *shard_elems (if not NULL) = S; when
+ * out is not NULL, copies the runs (BFO_ERANGE if capacity < *nruns). */
+int bfo_plan_runs(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank, int layout,
+                  bfo_run *out, uint32_t capacity, uint32_t *nruns, uint64_t *shard_elems);
+
 /* Deterministic global grad norm of one shard ("04 · 多 GPU 与混合精度" §4:
  * grad_norm, then grad_scale = min(1, 1/grad_norm), i.e. clip to 1.0; under
  * ZeRO-1 this is the shard's part, which ranks would add before the root).
