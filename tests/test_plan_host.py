@@ -151,3 +151,20 @@ def test_plan_errors_match_oracle():
             rc_t, n = o.table_check(o.table(entries))
             rc_o = rc_t if rc_t != o.OK else o.shard_range(n, world, rank)[0]
             assert rc_o == want
+
+
+def test_plan_capacity_and_null_arguments():
+    lib = bfo.library()
+    import ctypes
+    arr = (bfo.BfoTensor * 2)()
+    arr[0].offset, arr[0].numel, arr[0].flags = 0, 8, 1
+    arr[1].offset, arr[1].numel, arr[1].flags = 8, 8, 0
+    cnt, S = ctypes.c_uint32(0), ctypes.c_uint64(0)
+    out = (bfo.BfoRun * 1)()
+    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, None, None) == o.EINVAL
+    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == o.OK
+    assert (cnt.value, S.value) == (2, 16)
+    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, out, 1, ctypes.byref(cnt), None) == o.ERANGE
+    assert lib.bfo_plan_runs(None, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), None) == o.EINVAL
+    assert lib.bfo_plan_runs(None, 0, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == o.OK
+    assert (cnt.value, S.value) == (0, 0)
