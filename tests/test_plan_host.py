@@ -161,10 +161,10 @@ def test_plan_capacity_and_null_arguments():
     arr[1].offset, arr[1].numel, arr[1].flags = 8, 8, 0
     cnt, S = ctypes.c_uint32(0), ctypes.c_uint64(0)
     out = (bfo.BfoRun * 1)()
-    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, None, None) == o.EINVAL
-    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == o.OK
+    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, None, None) == bfo.EINVAL
+    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == bfo.OK
     assert (cnt.value, S.value) == (2, 16)
-    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, out, 1, ctypes.byref(cnt), None) == o.ERANGE
-    assert lib.bfo_plan_runs(None, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), None) == o.EINVAL
-    assert lib.bfo_plan_runs(None, 0, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == o.OK
+    assert lib.bfo_plan_runs(arr, 2, 1, 0, bfo.LAYOUT_FLAT, out, 1, ctypes.byref(cnt), None) == bfo.ERANGE
+    assert lib.bfo_plan_runs(None, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), None) == bfo.EINVAL
+    assert lib.bfo_plan_runs(None, 0, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == bfo.OK
     assert (cnt.value, S.value) == (0, 0)
