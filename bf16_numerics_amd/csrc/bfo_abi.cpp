@@ -43,7 +43,9 @@ struct bfo_table_s {
     double *normPartials = nullptr;  // [normTiles(S) + normRuns(...)], at least 1
     uint64_t *normOffset = nullptr;  // [normTiles(S)], per-tensor tables only
 
-    bfo::ShardView view() const { return {tile, local, addr, rng, flag, normOffset}; }
+    bfo::ShardView view() const {
+        return {tile, local, addr, rng, flag, normOffset, layout == BFO_LAYOUT_FLAT ? begin : UINT64_MAX};
+    }
 };
 
 bfo::TableFacts bfo::tableFacts(const bfo_table_s *t) {

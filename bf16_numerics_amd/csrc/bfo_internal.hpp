@@ -54,6 +54,10 @@ struct ShardView {
     // and that difference is a multiple of 8, else kNoNormOffset.  Null for
     // flat tables (whose grads are shard-local anyway).
     const uint64_t *normOffset;
+    // Flat tables: the shard's first global index (shard element j is then
+    // params/grads position j and global index flatBegin + j); UINT64_MAX for
+    // per-tensor tables.
+    uint64_t flatBegin;
 };
 constexpr uint64_t kNoNormOffset = UINT64_MAX;
 

@@ -136,6 +136,15 @@ struct Place {
 
 __device__ __forceinline__ Place placeVector(const ShardView &sv, uint32_t tileWord, uint64_t j0, uint64_t S) {
     Place pl;
+    if (sv.flatBegin != UINT64_MAX && !(tileWord & kTileMixed)) {
+        // Flat table, tile inside one run: positions follow from j0 alone, so
+        // no lookup stands between the lane and its params/grads access.
+        pl.run = tileWord;
+        pl.inRun = j0 + 8 <= S;
+        pl.addr0 = j0;
+        pl.rng0 = sv.flatBegin + j0;
+        return pl;
+    }
     uint32_t k = tileWord & ~kTileMixed;
     uint64_t runEnd = UINT64_MAX;
     if (tileWord & kTileMixed) {
