@@ -362,6 +362,16 @@ def test_replay_rebuilds_bf16_bit_exactly():
         o.adamw_step(tbl, 0, P, G, M, m, v, hp, 1.0, t, seed, o.ROUND_SR)
     assert np.array_equal(o.master_to_bf16_sr(M, 0, (1337 << 32) | 3), P)
     assert not np.array_equal(o.master_to_bf16_sr(M, 0, (1337 << 32) | 2), P)
+    # The same on a shard that starts mid-buffer (rank 2 of 4): the rebuild
+    # must key its draws on the global index, as the update does.
+    rc, b, e = o.shard_range(w.n, 4, 2)
+    assert rc == o.OK and b > 0
+    Ps, Ms = P[b:e].copy(), M[b:e].copy()
+    ms, vs = np.zeros(e - b, np.float32), np.zeros(e - b, np.float32)
+    G = to_bf16_bits_torch((rs.standard_normal(e - b) * 1e-3).astype(np.float32))
+    o.adamw_step(tbl, b, Ps, G, Ms, ms, vs, hp, 1.0, 4, (1337 << 32) | 4, o.ROUND_SR)
+    assert np.array_equal(o.master_to_bf16_sr(Ms, b, (1337 << 32) | 4), Ps)
+    assert not np.array_equal(o.master_to_bf16_sr(Ms, 0, (1337 << 32) | 4), Ps)
 
 
 def test_shard_concatenation_is_bit_identical():
