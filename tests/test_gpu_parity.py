@@ -478,7 +478,7 @@ def test_stall16m_sr_tracks_master_rne_freezes(bfo):
 # --------------------------------------------------------------------- full sizes
 
 
-def full_size_step(bfo, w, rank, steps=1):
+def full_size_step(bfo, w, rank, steps=1, master=True, rounding=o.ROUND_SR):
     """One rank of a full-size workload in the layout the benchmark times:
     full-length P and G buffers (ZeRO-1), shard-local M, m, v."""
     ents = w.entries()
@@ -486,7 +486,7 @@ def full_size_step(bfo, w, rank, steps=1):
     b, e = T.begin, T.end
     S = e - b
     P_full = torch.empty(w.n if w.world > 1 else 0, dtype=torch.bfloat16, device=DEV)
-    P, M, m, v = W.init_state(torch, w, b, e, DEV)
+    P, M, m, v = W.init_state(torch, w, b, e, DEV, master=master)
     if w.world > 1:
         P_full.view(torch.int16).fill_(0x7FA5)                             # sentinel NaN pattern
         P_full[b:e] = P
@@ -501,13 +501,13 @@ def full_size_step(bfo, w, rank, steps=1):
         W.fill_grads(torch, w, G, b, t)
         pre = [host_copy(st, lo - b, hi - b) for lo, hi in wins]
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
-        bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, t, step_seed(t), scale=res)
+        bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, t, step_seed(t), scale=res, rounding=rounding)
         got_norm = bfo.read_norm_result(res)
         Gh = G.cpu().view(torch.int16).numpy().view(np.uint16)
         assert_norm_parity(got_norm, o.grad_norm(Gh, w.hparams.max_norm))
         del Gh
         for (lo, hi), h in zip(wins, pre):
-            oracle_step(tbl, lo, h, w.hparams, got_norm[2], t, step_seed(t))
+            oracle_step(tbl, lo, h, w.hparams, got_norm[2], t, step_seed(t), rounding)
             assert_state_parity(host_copy(st, lo - b, hi - b), h, f"{w.name} r{rank} [{lo},{hi}) t={t}")
     if w.world > 1:
         outside = torch.cat([P_full[:b], P_full[e:]]).view(torch.int16)
@@ -520,6 +520,15 @@ def test_full_size_gpt2_1p5b_shard(bfo):
     for rank in (1, 0, 2, 3, 4, 5, 6, 7):
         got = full_size_step(bfo, w, rank, steps=2 if rank == 1 else 1)
         print(f"gpt2_1p5b rank {rank}: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
+
+
+@pytest.mark.parametrize("master,rounding", [(False, o.ROUND_SR), (False, o.ROUND_RNE), (True, o.ROUND_RNE)])
+def test_full_size_gpt2_1p5b_shard_variants(bfo, master, rounding):
+    # The other update variants at the benchmark's size and shard: no master
+    # (old weights read from the bf16 params), round to nearest even.
+    w = W.gpt2_1p5b_shard()
+    got = full_size_step(bfo, w, w.rank, steps=2, master=master, rounding=rounding)
+    print(f"gpt2_1p5b rank {w.rank} master={master} rounding={rounding}: scale {got[2]:.6f}", flush=True)
 
 
 def test_full_size_llama7b(bfo):
