@@ -531,6 +531,28 @@ def test_full_size_gpt2_1p5b_shard_variants(bfo, master, rounding):
     print(f"gpt2_1p5b rank {w.rank} master={master} rounding={rounding}: scale {got[2]:.6f}", flush=True)
 
 
+def test_full_size_rebuild_gpt2_1p5b_shard(bfo):
+    # The resume rebuild at the benchmark's size and shard: after a step, the
+    # master and that step's seed give back the step's bf16 params bit for
+    # bit, and sampled windows equal the oracle's rebuild of the same master.
+    w = W.gpt2_1p5b_shard()
+    ents = w.entries()
+    T = bfo.Table(ents, w.world, w.rank)
+    b, e = T.begin, T.end
+    P, M, m, v = W.init_state(torch, w, b, e, DEV)
+    G = torch.empty(e - b, dtype=torch.bfloat16, device=DEV)
+    W.fill_grads(torch, w, G, b, 1)
+    res = bfo.new_norm_result(DEV)
+    bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
+    bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, 1, step_seed(1), scale=res)
+    P2 = torch.zeros_like(P)
+    bfo.master_to_bf16_sr(T, M, P2, step_seed(1))
+    assert torch.equal(P2.view(torch.int16), P.view(torch.int16))
+    for lo, hi in windows(ents, b, e, seed=5):
+        ref = o.master_to_bf16_sr(f32(M[lo - b:hi - b]), lo, step_seed(1))
+        assert np.array_equal(u16(P2[lo - b:hi - b]), ref), (lo, hi)
+
+
 def test_full_size_llama7b(bfo):
     w = W.llama7b()
     got = full_size_step(bfo, w, 0, steps=2)
