@@ -91,7 +91,7 @@ def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
                                                  sl(h["M"], r), h["m"][r[0]:r[1]], h["v"][r[0]:r[1]], hp,
                                                  scale, t, (1337 << 32) | t, rounding), parts))
             el = time.perf_counter() - t0
-            if el >= budget or steps >= 256:
+            if el >= budget or steps >= 4096:
                 return steps, el
 
     with ThreadPoolExecutor(1) as pool:
