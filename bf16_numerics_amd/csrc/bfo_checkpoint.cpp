@@ -66,40 +66,85 @@ std::string donePath(const char *dir, uint64_t step) {
     return std::string(dir) + name;
 }
 
-// Moves bytes between a device array and a file through a pinned buffer.
+// Moves bytes between a device array and a file through two pinned halves of
+// a staging buffer, so that the copy of one chunk overlaps the file I/O of
+// the other.  Every copy is queued on the caller's stream and waited for
+// through an event before its half is reused.
 struct Stage {
+    static constexpr size_t kHalf = kStageBytes / 2;
     char *buf = nullptr;
+    hipEvent_t done[2] = {nullptr, nullptr};
     hipStream_t stream = nullptr;
     hipError_t err = hipSuccess;
     ~Stage() {
+        // No copy may still target the buffer when it is freed (error paths
+        // can leave one queued).
+        if (buf) (void)hipStreamSynchronize(stream);
+        for (hipEvent_t &e : done)
+            if (e) (void)hipEventDestroy(e);
         if (buf) (void)hipHostFree(buf);
     }
     bool open(hipStream_t s) {
         stream = s;
-        err = hipHostMalloc(reinterpret_cast<void **>(&buf), kStageBytes, hipHostMallocDefault);
-        return err == hipSuccess;
+        if ((err = hipHostMalloc(reinterpret_cast<void **>(&buf), kStageBytes, hipHostMallocDefault)) != hipSuccess)
+            return false;
+        for (hipEvent_t &e : done)
+            if ((err = hipEventCreateWithFlags(&e, hipEventDisableTiming)) != hipSuccess) return false;
+        return true;
     }
+    char *half(int h) { return buf + size_t(h) * kHalf; }
+    // Device -> file: chunk k+1 is copied while chunk k is written.
     int write(FILE *f, const void *dev, uint64_t bytes) {
         const char *src = static_cast<const char *>(dev);
-        for (uint64_t off = 0; off < bytes; off += kStageBytes) {
-            const size_t len = size_t(bytes - off < kStageBytes ? bytes - off : kStageBytes);
-            if ((err = hipMemcpyAsync(buf, src + off, len, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
-                (err = hipStreamSynchronize(stream)) != hipSuccess)
-                return BFO_EHIP;
-            if (std::fwrite(buf, 1, len, f) != len) return BFO_EIO;
+        const uint64_t chunks = (bytes + kHalf - 1) / kHalf;
+        auto len = [&](uint64_t k) { return size_t(bytes - k * kHalf < kHalf ? bytes - k * kHalf : kHalf); };
+        auto fetch = [&](uint64_t k) {
+            const int h = int(k & 1);
+            if ((err = hipMemcpyAsync(half(h), src + k * kHalf, len(k), hipMemcpyDeviceToHost, stream)) != hipSuccess)
+                return false;
+            return (err = hipEventRecord(done[h], stream)) == hipSuccess;
+        };
+        if (chunks && !fetch(0)) return BFO_EHIP;
+        for (uint64_t k = 0; k < chunks; ++k) {
+            const int h = int(k & 1);
+            if ((err = hipEventSynchronize(done[h])) != hipSuccess) return BFO_EHIP;
+            if (k + 1 < chunks && !fetch(k + 1)) return BFO_EHIP;
+            if (std::fwrite(half(h), 1, len(k), f) != len(k)) return BFO_EIO;
         }
         return BFO_OK;
     }
+    // File -> device: chunk k+1 is read while chunk k is copied.
     int read(FILE *f, void *dev, uint64_t bytes) {
         char *dst = static_cast<char *>(dev);
-        for (uint64_t off = 0; off < bytes; off += kStageBytes) {
-            const size_t len = size_t(bytes - off < kStageBytes ? bytes - off : kStageBytes);
-            if (std::fread(buf, 1, len, f) != len) return BFO_EFORMAT;
-            if ((err = hipMemcpyAsync(dst + off, buf, len, hipMemcpyHostToDevice, stream)) != hipSuccess ||
-                (err = hipStreamSynchronize(stream)) != hipSuccess)
-                return BFO_EHIP;
+        const uint64_t chunks = (bytes + kHalf - 1) / kHalf;
+        int rc = BFO_OK;
+        bool pending[2] = {false, false};
+        for (uint64_t k = 0; k < chunks && rc == BFO_OK; ++k) {
+            const int h = int(k & 1);
+            const size_t n = size_t(bytes - k * kHalf < kHalf ? bytes - k * kHalf : kHalf);
+            if (pending[h] && (err = hipEventSynchronize(done[h])) != hipSuccess) {
+                rc = BFO_EHIP;
+                break;
+            }
+            pending[h] = false;
+            if (std::fread(half(h), 1, n, f) != n) {
+                rc = BFO_EFORMAT;
+                break;
+            }
+            if ((err = hipMemcpyAsync(dst + k * kHalf, half(h), n, hipMemcpyHostToDevice, stream)) != hipSuccess ||
+                (err = hipEventRecord(done[h], stream)) != hipSuccess) {
+                rc = BFO_EHIP;
+                break;
+            }
+            pending[h] = true;
         }
-        return BFO_OK;
+        // Both halves must be idle before the buffer can be freed or reused.
+        const hipError_t e = hipStreamSynchronize(stream);
+        if (rc == BFO_OK && e != hipSuccess) {
+            err = e;
+            rc = BFO_EHIP;
+        }
+        return rc;
     }
 };
 
