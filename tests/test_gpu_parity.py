@@ -12,7 +12,7 @@ import torch
 
 import oracle as o
 from bf16_numerics_amd import workloads as W
-from gpu_harness import (SEED, assert_bf16_parity, assert_f32_parity, assert_norm_parity,
+from gpu_harness import (assert_bf16_parity, assert_f32_parity, assert_norm_parity,
                          assert_state_parity, dev_bf16, dev_f32, device_state, f32, host_copy,
                          oracle_hparams, oracle_step, step_seed, u16)
 

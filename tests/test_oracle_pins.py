@@ -8,7 +8,6 @@ import math
 from fractions import Fraction
 
 import numpy as np
-import pytest
 import torch
 
 import oracle as o
