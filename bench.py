@@ -161,13 +161,16 @@ def rebuild_rate(torch, bfo, stream, T, M, P, seed, launches):
             "algorithmic_bytes_per_launch": REBUILD_BYTES * M.numel()}
 
 
-def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs):
+def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs, norm=None, grads=None,
+                   ms_step=None):
     """Achievable bandwidth for the update's own traffic on this device: the
     library's stream-mix kernel (the update's bytes per element -- 14 read and
     14 written with a master, 12 and 10 without -- in its vector and
     workgroup plan, no arithmetic; key 0 leaves m, v and the master
     unchanged), timed per launch with HIP events on the launch stream, as the
-    update is."""
+    update is.  With `norm` (enqueues the real grad norm of grads[k]) it also
+    times K steps of norm + stream mix over the same grads, back to back like
+    the timed region: the step's own ceiling."""
     for _ in range(2):
         bfo.stream_mix(P, G, M, m, v, 0)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
@@ -179,9 +182,23 @@ def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs):
     ms = sum(a.elapsed_time(z) for a, z in evs) / launches
     per = UPDATE_BYTES if M is not None else UPDATE_BYTES_NO_MASTER
     gbs = per * m.numel() / (ms * 1e-3) / 1e9
-    return {"kernel": "streamMixKernel (update traffic, no arithmetic)", "achieved": round(gbs, 1),
-            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms, 5),
-            "update_over_ceiling": round(update_gbs / gbs, 4)}
+    out = {"kernel": "streamMixKernel (update traffic, no arithmetic)", "achieved": round(gbs, 1),
+           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms, 5),
+           "update_over_ceiling": round(update_gbs / gbs, 4)}
+    if norm is not None:
+        n = m.numel()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for k in range(launches):
+            norm(k)
+            bfo.stream_mix(P, grads[k % len(grads)][:n], M, m, v, 0)
+        z.record(stream)
+        torch.cuda.synchronize()
+        step_ms = a.elapsed_time(z) / launches
+        out["step_ms"] = round(step_ms, 5)
+        out["step_over_ceiling"] = round(step_ms / ms_step, 4)
+    return out
 
 
 def main():
@@ -412,7 +429,10 @@ def main():
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
         out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds, args.rounding == "sr")
     if not args.no_ceiling:
-        out["ceiling"] = stream_ceiling(torch, bfo, stream, P[:S], pool[0][:S], M, m, v, args.steps, achieved)
+        out["ceiling"] = stream_ceiling(
+            torch, bfo, stream, P[:S], pool[0][:S], M, m, v, args.steps, achieved,
+            norm=lambda k: bfo.grad_global_norm(T, pool[k % len(pool)], res, w.hparams.max_norm),
+            grads=pool, ms_step=ms_step)
     print(json.dumps(out), flush=True)
 
 
