@@ -32,6 +32,8 @@ constexpr uint64_t kNormTileVecs = uint64_t(kBlock) * kNormVecPerLane;
 constexpr int kNormFinishBlock = 1024;
 constexpr uint64_t kNormFinishDirect = 32768;
 constexpr uint64_t kNormReduceRun = 4096;
+// Shards of at most this many tiles run both stages in one workgroup.
+constexpr uint32_t kNormSmallTiles = 8;
 
 inline uint64_t normTiles(uint64_t S) { return ((S + 7) / 8 + kNormTileVecs - 1) / kNormTileVecs; }
 inline uint64_t normRuns(uint64_t ntiles) {

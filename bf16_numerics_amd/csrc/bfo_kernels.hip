@@ -510,23 +510,28 @@ __device__ __forceinline__ double blockSum(double x) {
     return total;
 }
 
-// One tile of stage 1 when the tile's grads sit at consecutive positions
-// starting 16-byte aligned (shard element j at base[j]): a lane's address
-// needs no plan lookup (two dependent loads that would stand before every
-// grad load and cost a quarter of the bandwidth).  Same lane-to-vector map
-// and order of additions as the plan path, hence the same bits.
-__device__ __forceinline__ double normTileDirect(const uint16_t *__restrict__ base, uint64_t S, uint64_t tile) {
+// The per-lane part of stage 1 for one tile: `lane` (0..255) takes vectors
+// lane, lane + 256, lane + 512, lane + 768 of the tile and adds the squares in
+// that order.  Every stage-1 path below runs these functions and reduces the
+// 256 lanes with tileSum, so they all give the same bits for the same tile.
+//
+// normTileDirect: the tile's grads sit at consecutive positions starting
+// 16-byte aligned (shard element j at base[j]), so a lane's address needs no
+// plan lookup (two dependent loads that would stand before every grad load
+// and cost a quarter of the bandwidth).
+__device__ __forceinline__ double normTileDirect(const uint16_t *__restrict__ base, uint64_t S, uint64_t tile,
+                                                 uint32_t lane) {
     const uint64_t full = S / 8;  // vectors with all eight elements in the shard
     uint4 x[kNormVecPerLane];
 #pragma unroll
     for (int k = 0; k < kNormVecPerLane; ++k) {
-        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + lane;
         if (q < full) x[k] = reinterpret_cast<const uint4 *>(base)[q];
     }
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < kNormVecPerLane; ++k) {
-        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + lane;
         if (q < full) {
             acc = sumSquares8(acc, x[k]);
         } else if (q * 8 < S) {
@@ -539,38 +544,20 @@ __device__ __forceinline__ double normTileDirect(const uint16_t *__restrict__ ba
     return acc;
 }
 
-// Flat shards with 16-byte-aligned grads: shard element j is grads[j].
-__global__ __launch_bounds__(kBlock) void normStage1FlatKernel(const uint16_t *__restrict__ G, uint64_t S,
-                                                               double *__restrict__ partials, uint64_t tileBase,
-                                                               uint64_t lastTile) {
-    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
-    const double total = blockSum<kBlock>(normTileDirect(G, S, tile));
-    if (threadIdx.x == 0) partials[tile] = total;
-}
-
-// Workgroups take tiles from the shard's end backwards: the partial of a tile
-// depends only on its index, so the order changes no bit of the result, and the
-// lines read last (the shard's start) are the ones the update, which walks
-// forward, reads first while they may still sit in the memory-side cache.
-__global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G, uint64_t S,
-                                                           ShardView sv, int pgVec,
-                                                           double *__restrict__ partials, uint64_t tileBase,
-                                                           uint64_t lastTile) {
-    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
-    // A tile wholly inside one run whose grads start 16-byte aligned: element
-    // j sits at grads[j + offset] for one offset, so read it directly.
+// normTilePlanned: the general case -- each vector is placed through the
+// shard plan (per-tensor tables, grads that are not 16-byte aligned), except
+// that a per-tensor tile inside one run with 16-byte-aligned grads sits at a
+// per-tile offset and goes direct.
+__device__ __forceinline__ double normTilePlanned(const uint16_t *__restrict__ G, uint64_t S, const ShardView &sv,
+                                                  int pgVec, uint64_t tile, uint32_t lane) {
     const uint64_t offset = (sv.normOffset && pgVec) ? sv.normOffset[tile] : kNoNormOffset;
-    if (offset != kNoNormOffset) {
-        const double total = blockSum<kBlock>(normTileDirect(G + offset, S, tile));
-        if (threadIdx.x == 0) partials[tile] = total;
-        return;
-    }
+    if (offset != kNoNormOffset) return normTileDirect(G + offset, S, tile, lane);
     uint4 x[kNormVecPerLane];
     Place pl[kNormVecPerLane];
     int mode[kNormVecPerLane];
 #pragma unroll
     for (int k = 0; k < kNormVecPerLane; ++k) {
-        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + lane;
         mode[k] = kNone;
         if (q * 8 >= S) continue;
         pl[k] = placeVector(sv, sv.tile[q / kTileVecs], q * 8, S);
@@ -590,7 +577,7 @@ __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__res
         if (mode[k] == kRegular || mode[k] == kSemi) {
             acc = sumSquares8(acc, x[k]);
         } else if (mode[k] == kPerElement) {
-            const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+            const uint64_t q = tile * kNormTileVecs + uint64_t(k) * kBlock + lane;
             uint32_t run = pl[k].run;
             for (int e = 0; e < 8; ++e) {
                 const uint64_t j = q * 8 + uint64_t(e);
@@ -602,8 +589,82 @@ __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__res
             }
         }
     }
-    const double total = blockSum<kBlock>(acc);
+    return acc;
+}
+
+// The tile's partial from its 256 lanes (four waves): butterfly within each
+// wave, then the four wave sums added in wave order by the group's first
+// lane.  `waveSums` holds one slot per wave of the workgroup; `group` is the
+// 256-lane group of the workgroup that worked on the tile.  Every lane of the
+// workgroup must call it (it synchronises the workgroup).
+__device__ __forceinline__ double tileSum(double x, double *waveSums, uint32_t group) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    if ((threadIdx.x & 63) == 0) waveSums[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double total = waveSums[group * 4];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) total += waveSums[group * 4 + w];
+    return total;
+}
+
+// Flat shards with 16-byte-aligned grads: shard element j is grads[j].
+__global__ __launch_bounds__(kBlock) void normStage1FlatKernel(const uint16_t *__restrict__ G, uint64_t S,
+                                                               double *__restrict__ partials, uint64_t tileBase,
+                                                               uint64_t lastTile) {
+    __shared__ double waveSums[kBlock / 64];
+    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
+    const double total = tileSum(normTileDirect(G, S, tile, threadIdx.x), waveSums, 0);
     if (threadIdx.x == 0) partials[tile] = total;
+}
+
+// Workgroups take tiles from the shard's end backwards: the partial of a tile
+// depends only on its index, so the order changes no bit of the result, and the
+// lines read last (the shard's start) are the ones the update, which walks
+// forward, reads first while they may still sit in the memory-side cache.
+__global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G, uint64_t S,
+                                                           ShardView sv, int pgVec,
+                                                           double *__restrict__ partials, uint64_t tileBase,
+                                                           uint64_t lastTile) {
+    __shared__ double waveSums[kBlock / 64];
+    const uint64_t tile = lastTile - (tileBase + blockIdx.x);
+    const double total = tileSum(normTilePlanned(G, S, sv, pgVec, tile, threadIdx.x), waveSums, 0);
+    if (threadIdx.x == 0) partials[tile] = total;
+}
+
+// Shards of at most kNormSmallTiles tiles: both stages in one 1024-lane
+// workgroup, so a small step pays one launch for its norm instead of two.
+// Each 256-lane group computes a tile's partial exactly as stage 1 does (same
+// lane map, same tileSum), the partials wait in LDS, and the final sum runs
+// the stage-2 code on them (lane t adds partial t to 0, then the block sum):
+// the bits equal those of the two-kernel path.
+__global__ __launch_bounds__(kNormFinishBlock) void normSmallKernel(const uint16_t *__restrict__ G, uint64_t S,
+                                                                    ShardView sv, int pgVec, int flat,
+                                                                    uint32_t ntiles, float maxNorm,
+                                                                    bfo_norm_result *__restrict__ out) {
+    __shared__ double waveSums[kNormFinishBlock / 64];
+    __shared__ double partial[kNormSmallTiles];
+    constexpr uint32_t kGroups = kNormFinishBlock / kBlock;
+    const uint32_t group = threadIdx.x / kBlock, lane = threadIdx.x % kBlock;
+    for (uint32_t base = 0; base < ntiles; base += kGroups) {
+        const uint32_t tile = base + group;
+        double acc = 0.0;
+        if (tile < ntiles)
+            acc = (flat && pgVec) ? normTileDirect(G, S, tile, lane) : normTilePlanned(G, S, sv, pgVec, tile, lane);
+        const double total = tileSum(acc, waveSums, group);
+        if (lane == 0 && tile < ntiles) partial[tile] = total;
+        __syncthreads();  // partial written; waveSums free for the next round
+    }
+    double acc = 0.0;
+    if (threadIdx.x < ntiles) acc += partial[threadIdx.x];
+    const double sumsq = blockSum<kNormFinishBlock>(acc);
+    if (threadIdx.x == 0) {
+        const float norm = float(sqrt(sumsq));
+        const float scale = norm > maxNorm ? maxNorm / norm : 1.0f;
+        out->sumsq = sumsq;
+        out->norm = norm;
+        out->scale = scale;
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void normReduceKernel(const double *__restrict__ in, uint64_t count,
@@ -772,6 +833,11 @@ hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, floa
 hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, bool flat, float maxNorm,
                       double *partials, bfo_norm_result *out, hipStream_t stream) {
     const uint64_t ntiles = normTiles(S);
+    if (ntiles > 0 && ntiles <= kNormSmallTiles) {
+        hipLaunchKernelGGL(normSmallKernel, dim3(1), dim3(kNormFinishBlock), 0, stream, g, S, sv, pgVec,
+                           flat ? 1 : 0, uint32_t(ntiles), maxNorm, out);
+        return hipGetLastError();
+    }
     for (uint64_t base = 0; base < ntiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = ntiles - base < kMaxBlocksPerLaunch ? ntiles - base : kMaxBlocksPerLaunch;
         if (flat && pgVec)
