@@ -5,9 +5,13 @@ test checks a printed value, a closed form, an exact invariant, a library
 routine that the case reduces to, or brute force on a tiny input.
 """
 import math
+import os
+import shutil
+import subprocess
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 import oracle as o
@@ -29,11 +33,56 @@ def to_bf16_bits_torch(x32):
 # ---------------------------------------------------------------- Philox
 
 
-def test_philox_known_answers(golden):
-    for case in golden("philox4x32_10_kat.json")["cases"]:
-        ctr = [int(x, 16) for x in case["counter"]]
-        key = [int(x, 16) for x in case["key"]]
-        assert o.philox4x32_10(ctr, key) == [int(x, 16) for x in case["out"]]
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+ROCRAND_PHILOX = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+
+
+def rocrand_philox(cases, tmp_path):
+    """Philox4x32-10 output blocks of (counter, key) cases from rocRAND's own
+    implementation (tests/c/philox_rocrand.cpp, built host-only)."""
+    if not (os.path.exists(HIPCC) and os.path.exists(ROCRAND_PHILOX)):
+        pytest.skip("needs hipcc and the rocRAND headers")
+    exe = tmp_path / "philox_rocrand"
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "philox_rocrand.cpp")
+    subprocess.run([HIPCC, "-O1", "-x", "hip", "--offload-host-only", "-o", str(exe), src], check=True)
+    text = "".join(" ".join(f"{w:08x}" for w in list(c) + list(k)) + "\n" for c, k in cases)
+    r = subprocess.run([str(exe)], input=text, capture_output=True, text=True, timeout=120, check=True)
+    out = [[int(x, 16) for x in line.split()] for line in r.stdout.splitlines()]
+    assert len(out) == len(cases)
+    return out
+
+
+def test_philox_equals_rocrand(tmp_path):
+    # The oracle's generator against the library's on edge words, random
+    # counters and keys, and the counters the draws use: (index >> 3) split
+    # into two words around the 2^32 group boundary, keyed by step seeds.
+    m32 = 0xFFFFFFFF
+    cases = [((0, 0, 0, 0), (0, 0)), ((m32,) * 4, (m32, m32)), ((1, 0, 0, 0), (0, 0)), ((0, 0, 0, 1), (0, 0)),
+             ((0, 0, 0, 0), (1, 0)), ((0, 0, 0, 0), (0, 1)), ((0x80000000,) * 4, (0x80000000, 0x80000000))]
+    rs = np.random.default_rng(11)
+    cases += [(tuple(int(x) for x in rs.integers(0, 1 << 32, 4)), tuple(int(x) for x in rs.integers(0, 1 << 32, 2)))
+              for _ in range(200)]
+    for group in ((1 << 32) - 2, (1 << 32) - 1, 1 << 32, (1 << 32) + 1, 6_738_415_616 >> 3, (1 << 61) + 3):
+        for t in (1, 2, 1000):
+            seed = (1337 << 32) | t
+            cases.append(((group & m32, group >> 32, 0, 0), (seed & m32, seed >> 32)))
+    ref = rocrand_philox(cases, tmp_path)
+    for (c, k), want in zip(cases, ref):
+        assert o.philox4x32_10(list(c), list(k)) == want, (c, k)
+
+
+def test_rng16_draws_from_rocrand_blocks(tmp_path):
+    # Draw i is 16-bit half (i & 1) of word (i >> 1) & 3 of the block at
+    # counter (lo32(i >> 3), hi32(i >> 3), 0, 0), key (lo32(seed), hi32(seed)).
+    m32 = 0xFFFFFFFF
+    for first, count, seed in ((0, 64, 0), (5, 29, 0xDEADBEEF12345678), ((1 << 35) - 13, 40, (1337 << 32) | 3)):
+        groups = range(first >> 3, ((first + count - 1) >> 3) + 1)
+        blocks = rocrand_philox([((g & m32, g >> 32, 0, 0), (seed & m32, seed >> 32)) for g in groups], tmp_path)
+        want = []
+        for i in range(first, first + count):
+            word = blocks[(i >> 3) - (first >> 3)][(i >> 1) & 3]
+            want.append((word >> 16) if i & 1 else (word & 0xFFFF))
+        assert o.rng16(first, count, seed).tolist() == want, (first, count, seed)
 
 
 def test_rng16_uniform_chi_square():
