@@ -605,27 +605,28 @@ def test_full_size_gpt2_1p5b_eight_shards_equal_the_unsharded_step(bfo):
         print(f"t={t}: 8 shards == unsharded (n={n}), sumsq {glob:.6f}", flush=True)
 
 
-def test_full_size_gpt2_1p5b_per_tensor(bfo):
-    # llm.c's ZeRO-1 layout at full size: rank 1 of 8 owns 1/8 of each of the
-    # 580 tensors; P and G are the full 1.56e9-element buffers.  The oracle
-    # steps sampled windows of the shard (around every run start, the ends
-    # and random places) through the global index map.
-    w = W.gpt2_1p5b_shard()
+def per_tensor_full_size(bfo, w, world, rank, steps=2):
+    """llm.c's ZeRO-1 layout at full size: rank `rank` of `world` owns 1/world
+    of every tensor; P and G are the full n-element buffers.  The oracle
+    steps sampled windows of the shard (around every run start, the ends and
+    random places) through the global index map; the norm is compared over
+    the whole shard."""
     ents = w.entries()
     tbl = o.table(ents)
-    T = bfo.Table(ents, w.world, w.rank, layout=bfo.LAYOUT_PER_TENSOR)
+    T = bfo.Table(ents, world, rank, layout=bfo.LAYOUT_PER_TENSOR)
     S = T.size
-    gidx = _oracle_gidx(bfo, tbl, w, w.world, w.rank, bfo.LAYOUT_PER_TENSOR)
-    assert S == w.n // w.world and np.array_equal(T.global_index(), gidx)
-    P, M_full, _, _ = W.init_state(torch, w, 0, w.n, DEV)
+    gidx = _oracle_gidx(bfo, tbl, w, world, rank, bfo.LAYOUT_PER_TENSOR)
+    assert S == w.n // world and np.array_equal(T.global_index(), gidx)
+    P, M_full, m0, v0 = W.init_state(torch, w, 0, w.n, DEV)
+    del m0, v0
     gi = torch.from_numpy(gidx.astype(np.int64)).to(DEV)
     st = {"M": M_full[gi].clone(), "m": torch.zeros(S, device=DEV), "v": torch.zeros(S, device=DEV)}
-    del M_full
+    del M_full, gi
     torch.cuda.empty_cache()
     G = torch.empty(w.n, dtype=torch.bfloat16, device=DEV)
     res = bfo.new_norm_result(DEV)
     wins = windows([(local, 0, 0) for local, *_ in T.runs()], 0, S, seed=3)
-    for t in (1, 2):
+    for t in range(1, steps + 1):
         W.fill_grads(torch, w, G, 0, t)
         Ph, Gh = u16(P), u16(G)
         pre = [{k: f32(st[k][lo:hi]) for k in ("M", "m", "v")} for lo, hi in wins]
@@ -638,12 +639,23 @@ def test_full_size_gpt2_1p5b_per_tensor(bfo):
             o.adamw_step_mapped(tbl, g, Ph, Gh, h["M"], h["m"], h["v"], oracle_hparams(w.hparams), got[2], t,
                                 step_seed(t))
             gpu = u16(P[torch.from_numpy(g.astype(np.int64)).to(DEV)])
-            assert_bf16_parity(gpu, Ph[g], f"per-tensor 1.5B [{lo},{hi}) t={t} params")
+            assert_bf16_parity(gpu, Ph[g], f"per-tensor {w.name} [{lo},{hi}) t={t} params")
             for k in ("M", "m", "v"):
-                assert_f32_parity(f32(st[k][lo:hi]), h[k], f"per-tensor 1.5B [{lo},{hi}) t={t} {k}")
+                assert_f32_parity(f32(st[k][lo:hi]), h[k], f"per-tensor {w.name} [{lo},{hi}) t={t} {k}")
         del Ph, Gh
-        print(f"gpt2_1p5b per-tensor rank {w.rank}, t={t}: norm {got[1]:.6f} scale {got[2]:.6f}, "
+        print(f"{w.name} per-tensor rank {rank} of {world}, t={t}: norm {got[1]:.6f} scale {got[2]:.6f}, "
               f"{len(wins)} windows", flush=True)
+
+
+def test_full_size_gpt2_1p5b_per_tensor(bfo):
+    w = W.gpt2_1p5b_shard()
+    per_tensor_full_size(bfo, w, w.world, w.rank)
+
+
+def test_full_size_llama7b_per_tensor_last_rank(bfo):
+    # Rank 7 of 8 holds the last eighth of every tensor: its positions in the
+    # 6.74e9-element params and grads run past 2^32 and 2^32 - 1 bytes.
+    per_tensor_full_size(bfo, W.llama7b(), 8, 7)
 
 
 # --------------------------------------------------------------------- layouts
