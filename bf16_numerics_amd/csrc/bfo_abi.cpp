@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <vector>
 
@@ -19,6 +20,27 @@ thread_local int gLastHipError = 0;
 int hipFail(hipError_t e) { return bfo::recordHipFailure(e); }
 
 bool alignedTo(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The byte range [lo, hi) an array argument covers; a null pointer covers
+// nothing.
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span(const void *p, uint64_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(p);
+    if (!p) return {0, 0};
+    return {x, bytes > UINTPTR_MAX - x ? UINTPTR_MAX : x + uintptr_t(bytes)};
+}
+
+// True when two of the arrays of one call share a byte: the kernels read and
+// write them as distinct (restrict) buffers.
+bool anyOverlap(std::initializer_list<Span> spans) {
+    for (const Span *a = spans.begin(); a != spans.end(); ++a)
+        for (const Span *b = a + 1; b != spans.end(); ++b)
+            if (a->lo < a->hi && b->lo < b->hi && a->lo < b->hi && b->lo < a->hi) return true;
+    return false;
+}
 
 }  // namespace
 
@@ -47,6 +69,10 @@ struct bfo_table_s {
         return {tile, local, addr, rng, flag, normOffset, layout == BFO_LAYOUT_FLAT ? begin : UINT64_MAX};
     }
 };
+
+// Elements of the params and grads arrays a call addresses: the shard for
+// flat tables, the whole buffer for per-tensor ones.
+static uint64_t pgElems(const bfo_table_s *t) { return t->layout == BFO_LAYOUT_FLAT ? t->S : t->n; }
 
 bfo::TableFacts bfo::tableFacts(const bfo_table_s *t) {
     return {t->n, t->S, t->world, t->rank, t->layout, t->fingerprint, t->runs.data(), uint32_t(t->runs.size())};
@@ -320,6 +346,7 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo
                      void *stream) {
     if (!table || !out || (table->S && !grads)) return BFO_EINVAL;
     if (!alignedTo(grads, 2) || !alignedTo(out, 16)) return BFO_EMISALIGNED;
+    if (anyOverlap({span(grads, 2 * pgElems(table)), span(out, sizeof(bfo_norm_result))})) return BFO_EINVAL;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
     hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0,
@@ -338,6 +365,10 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
     if (!alignedTo(params, 2) || !alignedTo(grads, 2) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
         !alignedTo(v, 16) || !alignedTo(scale, 4) || !alignedTo(skip, 4))
         return BFO_EMISALIGNED;
+    const uint64_t pg = 2 * pgElems(table);
+    if (anyOverlap({span(params, pg), span(grads, pg), span(master, 4 * S), span(m, 4 * S), span(v, 4 * S),
+                    span(scale, 4), span(skip, 4)}))
+        return BFO_EINVAL;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
     if (S == 0) return BFO_OK;
@@ -365,6 +396,7 @@ int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, ui
     const uint64_t S = table->S;
     if (S && (!master || !params)) return BFO_EINVAL;
     if (!alignedTo(master, 16) || !alignedTo(params, 2)) return BFO_EMISALIGNED;
+    if (anyOverlap({span(master, 4 * S), span(params, 2 * pgElems(table))})) return BFO_EINVAL;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
     if (S == 0) return BFO_OK;

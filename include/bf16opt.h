@@ -36,8 +36,10 @@
  *   - Memory.  Array arguments are device pointers on the device the table
  *     was created on.  master, m and v must be 16-byte aligned; params and
  *     grads 2-byte aligned (16-byte aligned pointers take the fastest path).
- *     Scalars and the hyperparameter struct are host memory.  The caller owns
- *     every buffer; the library keeps no pointer after a call returns.
+ *     The arrays of one call must not overlap one another (BFO_EINVAL): the
+ *     kernels read and write them as distinct buffers.  Scalars and the
+ *     hyperparameter struct are host memory.  The caller owns every buffer;
+ *     the library keeps no pointer after a call returns.
  *   - Asynchrony.  GPU work is queued on `stream` (a hipStream_t; NULL means
  *     the null stream) and the call returns without waiting for it.  Argument
  *     errors are reported synchronously and queue no work.  Apart from the
@@ -75,7 +77,7 @@ extern "C" {
 
 enum {
     BFO_OK = 0,
-    BFO_EINVAL = -1,        /* null pointer, world == 0, t == 0, unknown rounding mode */
+    BFO_EINVAL = -1,        /* null pointer, overlapping arrays, world == 0, t == 0, unknown rounding mode */
     BFO_ENOTDIVISIBLE = -2, /* n (or, per tensor, a tensor's size) is not a multiple of world */
     BFO_ERANGE = -3,        /* rank >= world */
     BFO_EMISALIGNED = -4,   /* pointer not aligned as required (see Memory above) */

@@ -444,6 +444,42 @@ def test_misaligned_and_wrong_size_rejected(bfo):
     assert e.value.status == bfo.EINVAL
 
 
+def test_overlapping_arrays_rejected(bfo):
+    # Arrays of one call that share bytes are refused before any work is
+    # queued; arrays that only touch (one ends where the next begins) are
+    # fine.
+    import ctypes
+    w = W.tiny()
+    n = w.n
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, n, DEV)
+    W.fill_grads(torch, w, st["G"], 0, 1)
+    both = torch.zeros(2 * n + 8, dtype=torch.float32, device=DEV)
+    before = {k: t.clone() for k, t in st.items()}
+    cases = [
+        (st["P"], st["P"], st["M"], st["m"], st["v"], None),          # params are the grads
+        (st["P"], st["G"], st["M"], both[:n], both[8:n + 8], None),   # m and v overlap
+        (st["P"], st["G"], st["m"], st["m"], st["v"], None),          # master is m
+        (st["P"], st["G"], st["M"], st["m"], st["v"], st["v"].data_ptr() + 64),  # scale inside v
+    ]
+    for P, G, M, m, v, scale in cases:
+        with pytest.raises(bfo.BfoError) as e:
+            bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, 1, 1, scale=scale)
+        assert e.value.status == bfo.EINVAL
+    lib, stream = bfo.library(), ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
+    g = ctypes.c_void_p(st["G"].data_ptr())
+    assert lib.grad_global_norm(T.handle, g, ctypes.c_float(1.0), g, stream) == bfo.EINVAL
+    mp = ctypes.c_void_p(st["M"].data_ptr())
+    assert lib.master_to_bf16_sr(T.handle, mp, mp, ctypes.c_uint64(1), stream) == bfo.EINVAL
+    torch.cuda.synchronize()
+    for k, t in st.items():
+        assert torch.equal(t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32),
+                           before[k].view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)), k
+    # touching, not overlapping: m and v as the two halves of one buffer
+    bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], both[:n], both[n:2 * n], w.hparams, 1, 1)
+    torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------- stall
 
 
