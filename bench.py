@@ -226,6 +226,9 @@ def main():
     ap.add_argument("--checkpoint-dir", default=None,
                     help="after timing, save this rank's state there, load it back, check it bit for bit, "
                          "time both and delete the files")
+    ap.add_argument("--graph", action="store_true",
+                    help="record the step once per grads buffer as a HIP graph (norm, outlier update, scheduled "
+                         "update, cursor advance) and time graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -307,21 +310,53 @@ def main():
             bfo.grad_global_norm(T, pool[k % len(pool)], res, w.hparams.max_norm)
             outlier.update(bfo.norm_ptr(res))
     skips = torch.zeros(1, dtype=torch.int64, device=dev)
+    sched = cursor = None
+    if args.graph:
+        # Per-step scalars for every step this run makes (the check pass
+        # included), read on the device through a cursor each update advances.
+        n_sched = last_t + args.steps
+        sched = bfo.step_schedule(hp, [(t, hps[min(t, last_t)].lr if hps else hp.lr, (1337 << 32) | t)
+                                       for t in range(1, n_sched + 1)], dev)
+        cursor = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def update(t, G, skip):
+        if args.graph:
+            bfo.adamw_sr_step_scheduled(T, P, G, M, m, v, hp, sched, cursor, scale=res, rounding=rounding,
+                                        skip=skip)
+        else:
+            bfo.adamw_sr_step(T, P, G, M, m, v, hps[t] if hps else hp, t, (1337 << 32) | t, scale=res,
+                              rounding=rounding, skip=skip)
+
+    def record_step(G):
+        bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
+        return outlier.update(bfo.norm_ptr(res)).skip if outlier is not None else None
+
+    graphs = []
+    if args.graph:
+        torch.cuda.synchronize()
+        for G in pool:                       # one graph per grads buffer; nothing else differs
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                update(None, G, record_step(G))
+                bfo.cursor_advance(cursor)
+            graphs.append(g)
+        torch.cuda.synchronize()
 
     def step(t, ev=None):
         G = pool[(t - 1) % len(pool)]
+        if graphs and ev is None:
+            graphs[(t - 1) % len(pool)].replay()
+            return
         if ev is not None:
             ev[2].record(stream)
-        bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
-        skip = None
-        if outlier is not None:
-            skip = outlier.update(bfo.norm_ptr(res)).skip
+        skip = record_step(G)
         if ev is not None:
             ev[0].record(stream)
-        bfo.adamw_sr_step(T, P, G, M, m, v, hps[t] if hps else hp, t, (1337 << 32) | t, scale=res,
-                          rounding=rounding, skip=skip)
+        update(t, G, skip)
         if ev is not None:
             ev[1].record(stream)
+        if args.graph:
+            bfo.cursor_advance(cursor)
 
     for t in range(1, args.warmup + 1):
         step(t)
@@ -372,7 +407,7 @@ def main():
     step_gbs = (upd_bytes + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
     achieved = upd_bytes * S / (upd_avg * 1e-3) / 1e9
     default_variant = (args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
-                       and args.rank is None)
+                       and args.rank is None and not args.graph)
     traffic = measured_traffic(w.name) if default_variant else None
     last_seed = (1337 << 32) | last_t      # seed of the last update (the check pass repeats the same t)
     sumsq, norm, scale = bfo.read_norm_result(res)
@@ -394,10 +429,10 @@ def main():
                    "layout": args.layout, "shard": [b, e], "shard_elems": S,
                    "world": w.world, "rank": w.rank, "tensors": len(w.tensors),
                    "grad_pool": len(pool), "bytes_per_param_step": upd_bytes + NORM_BYTES,
-                   "update": variant},
+                   "update": variant, "launch": "graph" if args.graph else "stream"},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": f"adamwTileKernel<{variant}>",
+        "roofline": {"bound": "hbm", "kernel": f"adamwTileKernel<{variant}{',scheduled' if args.graph else ''}>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": upd_bytes * S,

@@ -37,7 +37,8 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_decay_mask_dump", "bfo_status_string", "bfo_last_hip_error", "bfo_lr_at",
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
            "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
-           "bfo_stream_mix", "bfo_plan_runs")
+           "bfo_stream_mix", "bfo_plan_runs", "bfo_step_scalars_fill", "adamw_sr_step_scheduled",
+           "bfo_cursor_advance")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -64,7 +65,13 @@ class LrSchedule(ctypes.Structure):
                 ("decay_frac", ctypes.c_float), ("reserved2", ctypes.c_uint32)]
 
 
+class StepScalars(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("bc1", ctypes.c_float), ("bc2", ctypes.c_float),
+                ("reserved", ctypes.c_uint32), ("t", ctypes.c_uint64), ("seed", ctypes.c_uint64)]
+
+
 NORM_RESULT_BYTES = 16  # bfo_norm_result: double sumsq; float norm; float scale
+STEP_SCALARS_BYTES = 32
 
 
 class BfoError(RuntimeError):
@@ -113,6 +120,11 @@ def _lib():
         "bfo_stream_mix": (i32, [vp, vp, vp, vp, vp, u64, u32, vp]),
         "bfo_plan_runs": (i32, [ctypes.POINTER(BfoTensor), u32, u32, u32, i32, ctypes.POINTER(BfoRun), u32,
                                 ctypes.POINTER(u32), pu64]),
+        "bfo_step_scalars_fill": (i32, [ctypes.POINTER(AdamwHParams), u64, ctypes.c_float, u64,
+                                        ctypes.POINTER(StepScalars)]),
+        "adamw_sr_step_scheduled": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, u64, vp, vp,
+                                          vp, i32, vp]),
+        "bfo_cursor_advance": (i32, [vp, vp]),
         "bfo_status_string": (ctypes.c_char_p, [i32]),
         "bfo_last_hip_error": (i32, []),
     }
@@ -288,6 +300,17 @@ def grad_global_norm(table, grads, out, max_norm=1.0):
     return out
 
 
+def _scale_arg(scale, dev):
+    """A norm-result buffer (its .scale is used), an int device address, or None for 1.0."""
+    if isinstance(scale, torch.Tensor):
+        if scale.dtype != torch.float64 or scale.numel() != 2 or scale.device != dev:
+            raise ValueError("scale must be a norm-result buffer on the table's device")
+        return ctypes.c_void_p(scale_ptr(scale))
+    if scale is None:
+        return None
+    return ctypes.c_void_p(int(scale))
+
+
 def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
                   rounding=ROUND_SR, skip=None):
     """One fused AdamW step over the shard.  scale: a norm-result buffer
@@ -301,20 +324,66 @@ def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
     M = _arg(master, torch.float32, S, "master", dev)
     mm = _arg(m, torch.float32, S, "m", dev)
     vv = _arg(v, torch.float32, S, "v", dev)
-    if isinstance(scale, torch.Tensor):
-        if scale.dtype != torch.float64 or scale.numel() != 2 or scale.device != dev:
-            raise ValueError("scale must be a norm-result buffer on the table's device")
-        sp = ctypes.c_void_p(scale_ptr(scale))
-    elif scale is None:
-        sp = None
-    else:
-        sp = ctypes.c_void_p(int(scale))
+    sp = _scale_arg(scale, dev)
     sk = _arg(skip, torch.int32, 1, "skip", dev) if skip is not None else None
-    h = hp if isinstance(hp, AdamwHParams) else AdamwHParams(
-        hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1 if hp.bias_correction else 0)
+    h = _hparams(hp)
     with torch.cuda.device(dev):
         _check("adamw_sr_step", _lib().adamw_sr_step(table.handle, p, g, M, mm, vv, ctypes.byref(h), sp, sk,
                                                      t, seed, rounding, _stream(dev)))
+
+
+def _hparams(hp):
+    if isinstance(hp, AdamwHParams):
+        return hp
+    return AdamwHParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1 if hp.bias_correction else 0)
+
+
+def step_scalars(hp, t, lr, seed):
+    """The per-step scalars of step t (bfo_step_scalars_fill), as a StepScalars."""
+    out = StepScalars()
+    _check("bfo_step_scalars_fill", _lib().bfo_step_scalars_fill(ctypes.byref(_hparams(hp)), t, lr, seed,
+                                                                 ctypes.byref(out)))
+    return out
+
+
+def step_schedule(hp, steps, device):
+    """A device array of bfo_step_scalars for [(t, lr, seed), ...] (uint8 tensor, 32 bytes per step)."""
+    arr = (StepScalars * max(1, len(steps)))()
+    for k, (t, lr, seed) in enumerate(steps):
+        arr[k] = step_scalars(hp, t, lr, seed)
+    host = torch.frombuffer(bytearray(bytes(arr)[:STEP_SCALARS_BYTES * len(steps)]), dtype=torch.uint8)
+    return host.to(device)
+
+
+def adamw_sr_step_scheduled(table, params, grads, master, m, v, hp, steps, cursor, scale=None,
+                            rounding=ROUND_SR, skip=None):
+    """adamw_sr_step with lr, bias corrections and seed read on the device from
+    steps[cursor] (steps: step_schedule(...); cursor: an int64 device tensor of
+    one element).  Nothing passed here changes from step to step."""
+    dev = table.device
+    S = table.size
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
+    g = _arg(grads, torch.bfloat16, table.pg_size, "grads", dev)
+    M = _arg(master, torch.float32, S, "master", dev)
+    mm = _arg(m, torch.float32, S, "m", dev)
+    vv = _arg(v, torch.float32, S, "v", dev)
+    if steps.dtype != torch.uint8 or steps.numel() % STEP_SCALARS_BYTES or steps.device != dev \
+            or not steps.is_contiguous():
+        raise ValueError("steps must be step_schedule(...) on the table's device")
+    cur = _arg(cursor, torch.int64, 1, "cursor", dev)
+    sp = _scale_arg(scale, dev)
+    sk = _arg(skip, torch.int32, 1, "skip", dev) if skip is not None else None
+    with torch.cuda.device(dev):
+        _check("adamw_sr_step_scheduled", _lib().adamw_sr_step_scheduled(
+            table.handle, p, g, M, mm, vv, ctypes.byref(_hparams(hp)), ctypes.c_void_p(steps.data_ptr()),
+            steps.numel() // STEP_SCALARS_BYTES, cur, sp, sk, rounding, _stream(dev)))
+
+
+def cursor_advance(cursor):
+    """cursor += 1 on the device (an int64 tensor of one element)."""
+    c = _arg(cursor, torch.int64, 1, "cursor", cursor.device)
+    with torch.cuda.device(cursor.device):
+        _check("bfo_cursor_advance", _lib().bfo_cursor_advance(c, _stream(cursor.device)))
 
 
 def lr_at(kind, step, warmup_steps, total_steps, lr_max, final_frac=0.0, decay_frac=0.0):

@@ -338,6 +338,48 @@ int checkDevice(const bfo_table_s *t) {
     return dev == t->device ? BFO_OK : BFO_EDEVICE;
 }
 
+// "第 13 讲" §1.7: bias correction 1 - beta^t, formed in binary64 and
+// rounded once to binary32; 1 when correction is off.
+float biasCorrection(float beta, uint64_t t, int32_t on) {
+    return on ? float(1.0 - std::pow(double(beta), double(t))) : 1.0f;
+}
+
+bfo::StepScalars stepScalars(const bfo_adamw_hparams &hp, float lr, float bc1, float bc2) {
+    bfo::StepScalars s;
+    s.lr = lr;
+    s.beta1 = hp.beta1;
+    s.beta2 = hp.beta2;
+    s.eps = hp.eps;
+    s.wd = hp.weight_decay;
+    s.bc1 = bc1;
+    s.bc2 = bc2;
+    return s;
+}
+
+// Validation and launch shared by adamw_sr_step and adamw_sr_step_scheduled.
+int launchStep(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m, float *v,
+               const bfo::StepScalars &s, const float *scale, const int32_t *skip, uint64_t seed, int rounding,
+               const bfo::StepSchedule *sched, void *stream) {
+    if (!table) return BFO_EINVAL;
+    if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
+    const uint64_t S = table->S;
+    if (S && (!params || !grads || !m || !v)) return BFO_EINVAL;
+    if (!alignedTo(params, 2) || !alignedTo(grads, 2) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
+        !alignedTo(v, 16) || !alignedTo(scale, 4) || !alignedTo(skip, 4))
+        return BFO_EMISALIGNED;
+    const uint64_t pg = 2 * pgElems(table);
+    if (anyOverlap({span(params, pg), span(grads, pg), span(master, 4 * S), span(m, 4 * S), span(v, 4 * S),
+                    span(scale, 4), span(skip, 4)}))
+        return BFO_EINVAL;
+    int rc = checkDevice(table);
+    if (rc != BFO_OK) return rc;
+    if (S == 0) return BFO_OK;
+    const int pgVec = alignedTo(params, 16) && alignedTo(grads, 16) ? 1 : 0;
+    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, scale, skip, seed,
+                                     rounding, sched, static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
 }  // namespace
 
 extern "C" {
@@ -358,35 +400,46 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo
 int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
                   float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
                   uint64_t seed, int rounding, void *stream) {
-    if (!table || !hp || t == 0) return BFO_EINVAL;
-    if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
-    const uint64_t S = table->S;
-    if (S && (!params || !grads || !m || !v)) return BFO_EINVAL;
-    if (!alignedTo(params, 2) || !alignedTo(grads, 2) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
-        !alignedTo(v, 16) || !alignedTo(scale, 4) || !alignedTo(skip, 4))
-        return BFO_EMISALIGNED;
-    const uint64_t pg = 2 * pgElems(table);
-    if (anyOverlap({span(params, pg), span(grads, pg), span(master, 4 * S), span(m, 4 * S), span(v, 4 * S),
-                    span(scale, 4), span(skip, 4)}))
+    if (!hp || t == 0) return BFO_EINVAL;
+    bfo::StepScalars s = stepScalars(*hp, hp->lr, biasCorrection(hp->beta1, t, hp->bias_correction),
+                                     biasCorrection(hp->beta2, t, hp->bias_correction));
+    return launchStep(table, params, grads, master, m, v, s, scale, skip, seed, rounding, nullptr, stream);
+}
+
+int bfo_step_scalars_fill(const bfo_adamw_hparams *hp, uint64_t t, float lr, uint64_t seed,
+                          bfo_step_scalars *out) {
+    if (!hp || !out || t == 0) return BFO_EINVAL;
+    *out = bfo_step_scalars{};
+    out->lr = lr;
+    out->bc1 = biasCorrection(hp->beta1, t, hp->bias_correction);
+    out->bc2 = biasCorrection(hp->beta2, t, hp->bias_correction);
+    out->t = t;
+    out->seed = seed;
+    return BFO_OK;
+}
+
+int adamw_sr_step_scheduled(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                            float *v, const bfo_adamw_hparams *hp, const bfo_step_scalars *steps,
+                            uint64_t count, const uint64_t *cursor, const float *scale, const int32_t *skip,
+                            int rounding, void *stream) {
+    if (!hp || !steps || !cursor) return BFO_EINVAL;
+    if (!alignedTo(steps, 16) || !alignedTo(cursor, 8)) return BFO_EMISALIGNED;
+    const uint64_t S = table ? table->S : 0;
+    const uint64_t pg = table ? 2 * pgElems(table) : 0;
+    if (count > UINT64_MAX / sizeof(bfo_step_scalars) ||
+        anyOverlap({span(steps, count * sizeof(bfo_step_scalars)), span(params, pg), span(master, 4 * S),
+                    span(m, 4 * S), span(v, 4 * S)}) ||
+        anyOverlap({span(cursor, 8), span(params, pg), span(master, 4 * S), span(m, 4 * S), span(v, 4 * S)}))
         return BFO_EINVAL;
-    int rc = checkDevice(table);
-    if (rc != BFO_OK) return rc;
-    if (S == 0) return BFO_OK;
+    const bfo::StepSchedule sched{steps, count, cursor};
+    return launchStep(table, params, grads, master, m, v, stepScalars(*hp, 0.0f, 1.0f, 1.0f), scale, skip, 0,
+                      rounding, &sched, stream);
+}
 
-    // "第 13 讲" §1.7: bias corrections 1 - beta^t, formed in binary64 and
-    // rounded once to binary32; 1 when correction is off.
-    bfo::StepScalars s;
-    s.lr = hp->lr;
-    s.beta1 = hp->beta1;
-    s.beta2 = hp->beta2;
-    s.eps = hp->eps;
-    s.wd = hp->weight_decay;
-    s.bc1 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta1), double(t))) : 1.0f;
-    s.bc2 = hp->bias_correction ? float(1.0 - std::pow(double(hp->beta2), double(t))) : 1.0f;
-
-    const int pgVec = alignedTo(params, 16) && alignedTo(grads, 16) ? 1 : 0;
-    hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, scale, skip,
-                                     seed, rounding, static_cast<hipStream_t>(stream));
+int bfo_cursor_advance(uint64_t *cursor, void *stream) {
+    if (!cursor) return BFO_EINVAL;
+    if (!alignedTo(cursor, 8)) return BFO_EMISALIGNED;
+    hipError_t he = bfo::launchCursorAdvance(cursor, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 

@@ -67,6 +67,14 @@ struct StepScalars {
     float lr, beta1, beta2, eps, wd, bc1, bc2;
 };
 
+// Device-resident per-step scalars of a scheduled update: steps[*cursor]
+// (of count) replaces lr, bc1, bc2 and the seed at run time.
+struct StepSchedule {
+    const bfo_step_scalars *steps = nullptr;
+    uint64_t count = 0;
+    const uint64_t *cursor = nullptr;
+};
+
 // Records a failed HIP call for bfo_last_hip_error() and returns BFO_EHIP.
 int recordHipFailure(hipError_t e);
 
@@ -88,9 +96,11 @@ TableFacts tableFacts(const bfo_table_s *table);
 // use 16-byte accesses).
 hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, bool flat, float maxNorm,
                       double *partials, bfo_norm_result *out, hipStream_t stream);
+// sched: NULL for scalars passed by value (s, seed), else read on the device.
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
                        ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
-                       uint64_t seed, int rounding, hipStream_t stream);
+                       uint64_t seed, int rounding, const StepSchedule *sched, hipStream_t stream);
+hipError_t launchCursorAdvance(uint64_t *cursor, hipStream_t stream);
 hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
                               uint64_t seed, hipStream_t stream);
 hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out,

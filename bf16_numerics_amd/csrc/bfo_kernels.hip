@@ -229,15 +229,21 @@ __device__ void adamwElementwise(uint16_t *P, const uint16_t *G, float *M, float
 // [tile * kTileVecs, +kTileVecs); lane t takes vectors t and t + 256 of it,
 // so each load instruction of a wave covers 1 KiB (bf16) or 2 KiB (fp32) of
 // contiguous memory.  All loads of the run-aligned vectors are issued before
-// any math.
+// any math.  kScheduled: lr, bias corrections and seed come from
+// steps[*cursor] in device memory instead of the launch arguments, so one
+// recorded launch serves every step; the cursor is read before the data
+// loads are issued and the scalars after, so their round trips overlap.
 // ---------------------------------------------------------------------------
-template <bool kMaster, int kRound>
+template <bool kMaster, int kRound, bool kScheduled>
 __global__ __launch_bounds__(kBlock) void adamwTileKernel(
     uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
     float *__restrict__ Mom, float *__restrict__ Var, uint64_t S, ShardView sv, int pgVec, StepScalars s,
     const float *__restrict__ scalePtr, const int32_t *__restrict__ skipPtr, uint32_t key0, uint32_t key1,
-    uint64_t tileBase) {
+    uint64_t tileBase, const bfo_step_scalars *__restrict__ steps, uint64_t nsteps,
+    const uint64_t *__restrict__ cursor) {
     if (skipPtr && *skipPtr) return;  // step control decided to skip this update
+    uint64_t cur = 0;
+    if constexpr (kScheduled) cur = *cursor;
     const float scale = scalePtr ? *scalePtr : 1.0f;
     const uint64_t tile = tileBase + blockIdx.x;
     const uint32_t tileWord = sv.tile[tile];
@@ -274,6 +280,15 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
             gv[k] = load8Narrow(G + pl[k].addr0);
             if constexpr (!kMaster) pv[k] = load8Narrow(P + pl[k].addr0);
         }
+    }
+    if constexpr (kScheduled) {
+        if (cur >= nsteps) return;    // past the scheduled steps: no update (nothing stored yet)
+        const bfo_step_scalars st = steps[cur];
+        s.lr = st.lr;
+        s.bc1 = st.bc1;
+        s.bc2 = st.bc2;
+        key0 = uint32_t(st.seed);
+        key1 = uint32_t(st.seed >> 32);
     }
 
 #pragma unroll
@@ -814,18 +829,41 @@ __global__ __launch_bounds__(64) void outlierResetKernel(OutlierState *st, uint3
     st->pad = 0;
 }
 
-template <bool kMaster, int kRound>
+template <bool kMaster, int kRound, bool kScheduled>
 hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
                         ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
-                        uint64_t seed, hipStream_t stream) {
+                        uint64_t seed, const StepSchedule &sched, hipStream_t stream) {
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
     const uint64_t tiles = (S + kTileElems - 1) / kTileElems;
     for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL((adamwTileKernel<kMaster, kRound>), dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G,
-                           M, m, v, S, sv, pgVec, s, scale, skip, k0, k1, base);
+        hipLaunchKernelGGL((adamwTileKernel<kMaster, kRound, kScheduled>), dim3(uint32_t(nb)), dim3(kBlock), 0,
+                           stream, P, G, M, m, v, S, sv, pgVec, s, scale, skip, k0, k1, base, sched.steps,
+                           sched.count, sched.cursor);
     }
     return hipGetLastError();
+}
+
+template <bool kScheduled>
+hipError_t launchAdamwS(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
+                        ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
+                        uint64_t seed, int rounding, const StepSchedule &sched, hipStream_t stream) {
+    if (M) {
+        return rounding == BFO_ROUND_SR
+                   ? launchAdamwT<true, BFO_ROUND_SR, kScheduled>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed,
+                                                                  sched, stream)
+                   : launchAdamwT<true, BFO_ROUND_RNE, kScheduled>(P, G, M, m, v, S, sv, pgVec, s, scale, skip,
+                                                                   seed, sched, stream);
+    }
+    return rounding == BFO_ROUND_SR
+               ? launchAdamwT<false, BFO_ROUND_SR, kScheduled>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed,
+                                                               sched, stream)
+               : launchAdamwT<false, BFO_ROUND_RNE, kScheduled>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed,
+                                                                sched, stream);
+}
+
+__global__ __launch_bounds__(64) void cursorAdvanceKernel(uint64_t *cursor) {
+    if (threadIdx.x == 0) *cursor += 1;
 }
 
 }  // namespace
@@ -864,15 +902,15 @@ hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, bo
 
 hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
                        ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
-                       uint64_t seed, int rounding, hipStream_t stream) {
-    if (M) {
-        return rounding == BFO_ROUND_SR
-                   ? launchAdamwT<true, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream)
-                   : launchAdamwT<true, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream);
-    }
-    return rounding == BFO_ROUND_SR
-               ? launchAdamwT<false, BFO_ROUND_SR>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream)
-               : launchAdamwT<false, BFO_ROUND_RNE>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, stream);
+                       uint64_t seed, int rounding, const StepSchedule *sched, hipStream_t stream) {
+    if (sched) return launchAdamwS<true>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, 0, rounding, *sched, stream);
+    return launchAdamwS<false>(P, G, M, m, v, S, sv, pgVec, s, scale, skip, seed, rounding, StepSchedule{},
+                               stream);
+}
+
+hipError_t launchCursorAdvance(uint64_t *cursor, hipStream_t stream) {
+    hipLaunchKernelGGL(cursorAdvanceKernel, dim3(1), dim3(64), 0, stream, cursor);
+    return hipGetLastError();
 }
 
 hipError_t launchOutlierUpdate(OutlierState *state, const float *value, float threshold, float *z,

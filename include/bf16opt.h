@@ -231,6 +231,46 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
                   float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
                   uint64_t seed, int rounding, void *stream);
 
+/* The per-step scalars of adamw_sr_step, for a step whose launches are
+ * recorded once (HIP graph capture) and replayed every step: they are read
+ * from device memory when the step runs instead of being passed by value.
+ * ("04 · 多 GPU 与混合精度" §4: the learning rate and the step number change
+ * every step; "第 13 讲" §1.7: bias correction.)  32 bytes. */
+typedef struct {
+    float lr;
+    float bc1;          /* 1 - beta1^t as adamw_sr_step forms it (1 when correction is off) */
+    float bc2;          /* 1 - beta2^t, likewise */
+    uint32_t reserved;  /* 0 */
+    uint64_t t;         /* the 1-based step number these were formed for */
+    uint64_t seed;      /* the step's rounding seed */
+} bfo_step_scalars;
+
+/* Host only: *out = the scalars adamw_sr_step(hp with lr, t, seed) uses --
+ * bc1 and bc2 exactly as documented there.  hp->lr is ignored (lr is the
+ * step's rate, e.g. from bfo_lr_at).  BFO_EINVAL for a null pointer or
+ * t == 0. */
+int bfo_step_scalars_fill(const bfo_adamw_hparams *hp, uint64_t t, float lr, uint64_t seed,
+                          bfo_step_scalars *out);
+
+/* adamw_sr_step with its per-step scalars taken on the device at run time:
+ * the step uses steps[*cursor], where steps is a device array of `count`
+ * bfo_step_scalars (16-byte aligned) and cursor a device uint64 (8-byte
+ * aligned).  hp supplies beta1, beta2, eps and weight_decay; its lr and
+ * bias_correction are ignored (the scalars carry them).  A cursor at or past
+ * `count` makes the step change nothing, as a set skip flag does.  Every
+ * other argument is as in adamw_sr_step, and for the same scalars the result
+ * is the same bit for bit.  No argument varies from step to step, so a graph
+ * recorded from grad_global_norm, this call and bfo_cursor_advance replays
+ * step after step, the caller changing only the grads (and, if it likes,
+ * the steps array) between replays. */
+int adamw_sr_step_scheduled(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                            float *v, const bfo_adamw_hparams *hp, const bfo_step_scalars *steps,
+                            uint64_t count, const uint64_t *cursor, const float *scale, const int32_t *skip,
+                            int rounding, void *stream);
+
+/* *cursor += 1, on the device (one work-item), queued on stream. */
+int bfo_cursor_advance(uint64_t *cursor, void *stream);
+
 /* Resume-time rebuild ("04 · 多 GPU 与混合精度" §5.2): params at element j's
  * position = SR(master[j], r16(i, seed)) with the draws of adamw_sr_step, so
  * passing the seed of the update that produced `master` reproduces its

@@ -106,6 +106,33 @@ def test_entry_points_reject_null_table_and_bad_scalars(bfo):
     assert lib.bfo_stream_mix(None, None, None, None, None, 8, 0, None) == bfo.EINVAL
     p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(24)
     assert lib.bfo_stream_mix(p16, p16, p16, p16, p8, 8, 0, None) == bfo.EMISALIGNED
+    st = bfo.StepScalars()
+    assert lib.bfo_step_scalars_fill(ctypes.byref(hp), 0, 1e-3, 1, ctypes.byref(st)) == bfo.EINVAL
+    assert lib.bfo_step_scalars_fill(None, 1, 1e-3, 1, ctypes.byref(st)) == bfo.EINVAL
+    assert lib.bfo_step_scalars_fill(ctypes.byref(hp), 1, 1e-3, 1, None) == bfo.EINVAL
+    assert lib.adamw_sr_step_scheduled(None, None, None, None, None, None, ctypes.byref(hp), p16, 1, p16, None,
+                                       None, 0, None) == bfo.EINVAL
+    assert lib.adamw_sr_step_scheduled(None, None, None, None, None, None, ctypes.byref(hp), p8, 1, p16, None,
+                                       None, 0, None) == bfo.EMISALIGNED
+    assert lib.adamw_sr_step_scheduled(None, None, None, None, None, None, ctypes.byref(hp), p16, 1, None, None,
+                                       None, 0, None) == bfo.EINVAL
+    assert lib.bfo_cursor_advance(None, None) == bfo.EINVAL
+    assert lib.bfo_cursor_advance(ctypes.c_void_p(20), None) == bfo.EMISALIGNED
+
+
+def test_step_scalars_match_the_oracles_bias_corrections(bfo):
+    # The device-resident step scalars carry the same 1 - beta^t the
+    # by-value step forms; the oracle's bias corrections are pinned to the
+    # printed multipliers.
+    import oracle as o
+    for beta1, beta2 in ((0.9, 0.95), (0.9, 0.999), (0.8, 0.99)):
+        for t in (1, 2, 3, 10, 100, 1000, 123_457, 10 ** 9):
+            for on in (True, False):
+                hp = bfo.AdamwHParams(5e-4, beta1, beta2, 1e-8, 0.1, 1 if on else 0)
+                st = bfo.step_scalars(hp, t, 2.5e-4, (1337 << 32) | t)
+                assert (st.bc1, st.bc2) == o.bias_corrections(beta1, beta2, t, on), (beta1, beta2, t, on)
+                assert st.t == t and st.seed == (1337 << 32) | t and st.reserved == 0
+                assert st.lr == float(ctypes.c_float(2.5e-4).value)
 
 
 def test_binding_refuses_a_missing_library(tmp_path, monkeypatch):
