@@ -5,8 +5,11 @@
  *
  * Workload: a 3-tensor flat buffer of n = 2 * 15,401 elements (2-D, 1-D,
  * 2-D), rank 1 of 2, so the shard starts mid-tensor and ends ragged; three
- * steps with grads large enough that the clip scale is active.  Prints one
- * line per check and exits non-zero on the first mismatch. */
+ * steps with grads large enough that the clip scale is active, the rebuild,
+ * then three more steps replayed from a HIP graph recorded once through the
+ * HIP C API (grad_global_norm, adamw_sr_step_scheduled, bfo_cursor_advance),
+ * the grads refilled between replays.  Prints one line per check and exits
+ * non-zero on the first mismatch. */
 #include "bf16opt.h"
 
 #include <hip/hip_runtime_api.h>
@@ -172,6 +175,62 @@ int main(void) {
     const int rb_ok = memcmp(rebuilt, oP, S * 2) == 0 && memcmp(orebuilt, oP, S * 2) == 0;
     printf("%s master_to_bf16_sr rebuilds the last step's bf16 params (GPU and oracle)\n", rb_ok ? "ok  " : "FAIL");
     failures += !rb_ok;
+
+    /* steps 4..6 from a graph: per-step scalars in device memory, a cursor */
+    bfo_step_scalars hsteps[3];
+    for (int k = 0; k < 3; ++k) BFO_OK_(bfo_step_scalars_fill(&hp, 4 + k, hp.lr, (1337ull << 32) | (4 + k), &hsteps[k]));
+    bfo_step_scalars *dsteps;
+    uint64_t *dcursor;
+    HIP_OK(hipMalloc((void **)&dsteps, sizeof hsteps));
+    HIP_OK(hipMalloc((void **)&dcursor, sizeof(uint64_t)));
+    HIP_OK(hipMemcpy(dsteps, hsteps, sizeof hsteps, hipMemcpyHostToDevice));
+    HIP_OK(hipMemset(dcursor, 0, sizeof(uint64_t)));
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+    BFO_OK_(grad_global_norm(tb, dG, 1.0f, dres, stream));
+    BFO_OK_(adamw_sr_step_scheduled(tb, dP + b, dG, dM, dm, dv, &hp, dsteps, 3, dcursor, &dres->scale, NULL,
+                                    BFO_ROUND_SR, stream));
+    BFO_OK_(bfo_cursor_advance(dcursor, stream));
+    HIP_OK(hipStreamEndCapture(stream, &graph));
+    HIP_OK(hipGraphInstantiateWithFlags(&exec, graph, 0));
+    for (uint64_t t = 4; t <= 6; ++t) {
+        seed = (1337ull << 32) | t;
+        for (uint64_t j = 0; j < S; ++j) hG[j] = bf16_from(mix64((t << 40) ^ (b + j)), 0.02f);
+        HIP_OK(hipMemcpyAsync(dG, hG, S * 2, hipMemcpyHostToDevice, stream));
+        HIP_OK(hipGraphLaunch(exec, stream));
+        bfo_norm_result res;
+        HIP_OK(hipMemcpyAsync(&res, dres, sizeof res, hipMemcpyDeviceToHost, stream));
+        HIP_OK(hipStreamSynchronize(stream));
+        double osum;
+        float onorm, oscale;
+        oracle_grad_norm(hG, S, 1.0f, &osum, &onorm, &oscale);
+        const double rel = res.sumsq > osum ? (res.sumsq - osum) / osum : (osum - res.sumsq) / osum;
+        const int norm_ok = rel <= 1e-12 && res.scale < 1.0f;
+        printf("%s graph replay, step %llu: sumsq %.17g vs oracle %.17g\n", norm_ok ? "ok  " : "FAIL",
+               (unsigned long long)t, res.sumsq, osum);
+        failures += !norm_ok;
+        if (oracle_adamw_step(otab, 3, b, S, oP, hG, oM, om, ov, &ohp, res.scale, t, seed, BFO_ROUND_SR) != 0) {
+            printf("FAIL oracle_adamw_step\n");
+            return 1;
+        }
+    }
+    uint64_t cursor = 0;
+    HIP_OK(hipMemcpy(&cursor, dcursor, sizeof cursor, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gP, dP, n * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gM, dM, S * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gm, dm, S * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gv, dv, S * 4, hipMemcpyDeviceToHost));
+    const int graph_ok = cursor == 3 && memcmp(gP + b, oP, S * 2) == 0 && memcmp(gM, oM, S * 4) == 0 &&
+                         memcmp(gm, om, S * 4) == 0 && memcmp(gv, ov, S * 4) == 0 &&
+                         memcmp(gP, hP, b * 2) == 0 && memcmp(gP + e, hP + e, (n - e) * 2) == 0;
+    printf("%s after 3 graph replays: params, master, m, v equal the oracle's bit for bit, cursor %llu\n",
+           graph_ok ? "ok  " : "FAIL", (unsigned long long)cursor);
+    failures += !graph_ok;
+    HIP_OK(hipGraphExecDestroy(exec));
+    HIP_OK(hipGraphDestroy(graph));
+    HIP_OK(hipFree(dsteps));
+    HIP_OK(hipFree(dcursor));
 
     BFO_OK_(bfo_table_destroy(tb));
     HIP_OK(hipStreamDestroy(stream));

@@ -1,6 +1,7 @@
 """The whole step driven from plain C on the GPU (tests/c/step_gpu.c): HIP
-runtime C API for memory, the library's C ABI for every step, the CPU oracle
-for the check.  No Python or torch sits between the caller and the kernels."""
+runtime C API for memory and graph capture, the library's C ABI for every
+step, the CPU oracle for the check.  No Python or torch sits between the
+caller and the kernels."""
 import os
 import shutil
 import subprocess
@@ -29,4 +30,4 @@ def test_step_from_c_matches_the_oracle_bit_for_bit(tmp_path):
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
-    assert r.stdout.count("ok  ") == 8
+    assert r.stdout.count("ok  ") == 12
