@@ -703,19 +703,21 @@ __global__ __launch_bounds__(kBlock) void normReduceKernel(const double *__restr
 __global__ __launch_bounds__(kNormFinishBlock) void normStage2Kernel(const double *__restrict__ partials,
                                                                      uint64_t count, float maxNorm,
                                                                      bfo_norm_result *__restrict__ out) {
-    // Lane t adds partials t, t+1024, t+2048, ... in that order; eight loads
-    // are issued before their adds so the L2 round trips overlap.
-    double acc = 0.0;
-    uint64_t k = threadIdx.x;
-    constexpr int kAhead = 8;
-    for (; k + (kAhead - 1) * kNormFinishBlock < count; k += kAhead * kNormFinishBlock) {
-        double p[kAhead];
+    // Lane t adds partials t, t+1024, t+2048, ... in that order.  Up to
+    // kNormFinishDirect partials (all that launchNorm ever passes) are loaded
+    // at once, 32 per lane, so the whole read is one round trip; absent ones
+    // load as +0, which leaves the non-negative running sum unchanged.
+    constexpr int kPer = int(kNormFinishDirect / kNormFinishBlock);
+    double p[kPer];
 #pragma unroll
-        for (int j = 0; j < kAhead; ++j) p[j] = partials[k + uint64_t(j) * kNormFinishBlock];
-#pragma unroll
-        for (int j = 0; j < kAhead; ++j) acc += p[j];
+    for (int j = 0; j < kPer; ++j) {
+        const uint64_t k = threadIdx.x + uint64_t(j) * kNormFinishBlock;
+        p[j] = k < count ? partials[k] : 0.0;
     }
-    for (; k < count; k += kNormFinishBlock) acc += partials[k];
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) acc += p[j];
+    for (uint64_t k = threadIdx.x + kNormFinishDirect; k < count; k += kNormFinishBlock) acc += partials[k];
     const double sumsq = blockSum<kNormFinishBlock>(acc);
     if (threadIdx.x == 0) {
         const float norm = float(sqrt(sumsq));
