@@ -30,7 +30,7 @@ def test_bench_line_follows_the_contract():
     assert d["vs_baseline"] is None
     assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
     assert d["unit"] == "Gparams/s" and d["higher_is_better"] is True and d["data"] == "synthetic"
-    assert d["config"]["workload"] == "tiny_gpt_d32"
+    assert d["config"]["workload"] == "tiny_gpt_d32" and d["config"]["launch"] == "stream"
     assert abs(d["value"] - d["config"]["shard_elems"] / (d["ms_per_step"] * 1e-3) / 1e9) <= 1e-3 * d["value"] + 1e-3
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
@@ -40,6 +40,15 @@ def test_bench_line_follows_the_contract():
     assert cb["kind"] == "oracle" and cb["unit"] == "Gparams/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["sample"], str) and cb["sample"]
     assert d["ceiling"]["achieved"] > 0 and d["rebuild"]["achieved"] > 0
+
+
+def test_bench_graph_mode_line():
+    # --graph times replays of the recorded step; the line keeps the contract
+    # and names the launch mode and the scheduled kernel.
+    d = run_bench("--workload", "tiny_gpt_d32", "--steps", "20", "--warmup", "3", "--no-cpu-baseline", "--graph")
+    assert d["config"]["launch"] == "graph"
+    assert d["roofline"]["kernel"].endswith(",scheduled>") and d["roofline"]["traffic"] is None
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and "cpu_baseline" not in d
 
 
 def test_bench_refuses_more_than_one_gpu():
