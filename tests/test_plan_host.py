@@ -4,6 +4,7 @@ Small tables are expanded element by element; the full-size models are
 checked at every run boundary."""
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import oracle as o
 from bf16_numerics_amd import binding as bfo
@@ -168,3 +169,48 @@ def test_plan_capacity_and_null_arguments():
     assert lib.bfo_plan_runs(None, 2, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), None) == bfo.EINVAL
     assert lib.bfo_plan_runs(None, 0, 1, 0, bfo.LAYOUT_FLAT, None, 0, ctypes.byref(cnt), ctypes.byref(S)) == bfo.OK
     assert (cnt.value, S.value) == (0, 0)
+
+
+@st.composite
+def tables_and_shards(draw):
+    """A random table (0-12 tensors of 0-70 elements, random flags, some
+    sizes multiples of the shard count), a shard count, a rank and a layout."""
+    world = draw(st.integers(1, 9))
+    sizes = draw(st.lists(st.integers(0, 70), max_size=12))
+    if draw(st.booleans()):
+        sizes = [s * world for s in sizes]
+    flags = draw(st.lists(st.integers(0, 1), min_size=len(sizes), max_size=len(sizes)))
+    entries, off = [], 0
+    for numel, f in zip(sizes, flags):
+        entries.append((off, numel, f))
+        off += numel
+    rank = draw(st.integers(0, world - 1))
+    layout = draw(st.sampled_from([bfo.LAYOUT_FLAT, bfo.LAYOUT_PER_TENSOR]))
+    return entries, world, rank, layout
+
+
+@settings(max_examples=400, deadline=None)
+@given(tables_and_shards())
+def test_random_plans_match_the_oracle(case):
+    # Any table, shard count, rank and layout: the host plan either fails with
+    # the oracle's status or expands, element by element, to the oracle's
+    # global index map and decay mask, in maximal runs.
+    entries, world, rank, layout = case
+    tbl = o.table(entries)
+    n = sum(e[1] for e in entries)
+    rc, S, runs = bfo.plan_runs(entries, world, rank, layout)
+    if layout == bfo.LAYOUT_PER_TENSOR:
+        rc_o, gidx = o.shard_map_per_tensor(tbl, world, rank)
+    else:
+        rc_o, b, e = o.shard_range(n, world, rank)
+        gidx = np.arange(b, e, dtype=np.uint64) if rc_o == o.OK else None
+    assert rc == rc_o, (entries, world, rank, layout)
+    if rc != o.OK:
+        return
+    local, addr, glob, flag = expand(runs)
+    assert S == gidx.size
+    assert np.array_equal(local, np.arange(S, dtype=np.uint64))
+    assert np.array_equal(glob, gidx)
+    assert np.array_equal(addr, glob if layout == bfo.LAYOUT_PER_TENSOR else local)
+    assert np.array_equal(flag, o.decay_mask(tbl, 0, n)[gidx.astype(np.int64)] if n else flag)
+    assert_maximal(runs)
