@@ -201,6 +201,38 @@ def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs, norm
     return out
 
 
+ARENA_FRAC = 0.8               # spread placement: the arena covers this share of device memory
+
+
+def state_arrays(torch, bfo, dev, placement, n, g_len, n_grads, S, master, reserve):
+    """The step's device arrays: P (n bf16), G (n_grads * g_len bf16), M (S
+    fp32, or None), m and v (S fp32).
+
+    "packed": one allocation per array.  "spread": one arena covering most of
+    device memory, as a framework that preallocates its memory pool holds it,
+    with the five groups starting on successive 16 GiB boundaries
+    (bfo_spread_layout) so that at any element index the arrays lie in
+    different 16 GiB regions; the rest of the arena is what such a framework
+    would give its other buffers.  `reserve` bytes stay outside the arena for
+    input generation."""
+    specs = [("P", n, torch.bfloat16, 2), ("G", n_grads * g_len, torch.bfloat16, 2)]
+    specs += [("M", S, torch.float32, 4)] if master else []
+    specs += [("m", S, torch.float32, 4), ("v", S, torch.float32, 4)]
+    out = {"M": None, "arena_bytes": 0}
+    if placement == "packed":
+        for name, count, dt, _ in specs:
+            out[name] = torch.empty(count, dtype=dt, device=dev)
+        return out
+    offsets, needed = bfo.spread_layout([count * es for _, count, _, es in specs])
+    free, total_mem = torch.cuda.mem_get_info(dev)
+    size = max(needed, min(int(ARENA_FRAC * total_mem), free - reserve)) // 4096 * 4096
+    arena = torch.empty(size, dtype=torch.uint8, device=dev)
+    for (name, count, dt, es), off in zip(specs, offsets):
+        out[name] = arena[off:off + count * es].view(dt)
+    out["arena_bytes"] = size
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +261,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="record the step once per grads buffer as a HIP graph (norm, outlier update, scheduled "
                          "update, cursor advance) and time graph replays")
+    ap.add_argument("--placement", choices=("spread", "packed"), default="spread",
+                    help="spread: params, grads, master, m and v carved from one arena covering most of device "
+                         "memory, each starting on its own 16 GiB boundary (bfo_spread_layout); packed: one "
+                         "allocation per array")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -262,32 +298,34 @@ def main():
     table_ms = (time.perf_counter() - t0) * 1e3
     S = T.size
 
-    if layout == bfo.LAYOUT_PER_TENSOR:
-        # llm.c-style ZeRO-1: full-length bf16 params and grads, shard-local
-        # fp32 master/m/v for this rank's 1/N of every tensor.
-        P, M_full, _, _ = W.init_state(torch, w, 0, w.n, dev, master=not args.no_master)
-        gi = torch.from_numpy(T.global_index().astype("int64")).to(dev)
-        M = None if args.no_master else M_full[gi].clone()
-        del M_full, gi
-        m = torch.zeros(S, dtype=torch.float32, device=dev)
-        v = torch.zeros(S, dtype=torch.float32, device=dev)
+    # Device arrays: the full-length bf16 params (ZeRO-1: every rank holds
+    # them), the gradient buffers, and the shard's fp32 master, m and v.
+    per_tensor = layout == bfo.LAYOUT_PER_TENSOR
+    g_len, g_begin = (w.n, 0) if per_tensor else (S, T.begin)
+    n_grads = max(1, args.grad_pool)
+    g_stride = (g_len + 127) // 128 * 128          # each gradient buffer starts on a 256-byte line
+    reserve = (16 << 30) + g_len * 6 + (S * 8 if per_tensor else 0)   # grads generation, index map
+    arrays = state_arrays(torch, bfo, dev, args.placement, w.n, g_stride, n_grads, S, not args.no_master,
+                          reserve)
+    P_full, grads_all, M, m, v = (arrays[k] for k in ("P", "G", "M", "m", "v"))
+    if per_tensor:
+        # llm.c-style ZeRO-1: this rank's 1/N of every tensor.
+        P = P_full
+        W.init_params_into(torch, w, 0, P)
+        if M is not None:
+            M.copy_(P[torch.from_numpy(T.global_index().astype("int64")).to(dev)].to(torch.float32))
         b, e = 0, S
-        g_len, g_begin = w.n, 0
     else:
-        # Contiguous ZeRO-1 layout: full-length bf16 params, shard-local rest.
+        # Contiguous ZeRO-1 layout: the shard [b, e) of the params, the rest shard-local.
         b, e = T.begin, T.end
-        P_full = torch.empty(w.n if w.world > 1 else 0, dtype=torch.bfloat16, device=dev)
-        P, M, m, v = W.init_state(torch, w, b, e, dev, master=not args.no_master)
-        if w.world > 1:
-            P_full[b:e] = P
-            del P
-            P = P_full[b:e]
-        g_len, g_begin = S, b
-    pool = []
-    for k in range(max(1, args.grad_pool)):
-        G = torch.empty(g_len, dtype=torch.bfloat16, device=dev)
+        P = P_full[b:e]
+        W.init_params_into(torch, w, b, P, M)
+    m.zero_()
+    v.zero_()
+    pool = [grads_all[k * g_stride:k * g_stride + g_len] for k in range(n_grads)]
+    for k, G in enumerate(pool):
         W.fill_grads(torch, w, G, g_begin, k + 1)
-        pool.append(G)
+    torch.cuda.empty_cache()
     res = bfo.new_norm_result(dev)
     hp = bfo.AdamwHParams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
                           w.hparams.weight_decay, 1)
@@ -407,7 +445,7 @@ def main():
     step_gbs = (upd_bytes + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
     achieved = upd_bytes * S / (upd_avg * 1e-3) / 1e9
     default_variant = (args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
-                       and args.rank is None and not args.graph)
+                       and args.rank is None and not args.graph and args.placement == "spread")
     traffic = measured_traffic(w.name) if default_variant else None
     last_seed = (1337 << 32) | last_t      # seed of the last update (the check pass repeats the same t)
     sumsq, norm, scale = bfo.read_norm_result(res)
@@ -429,7 +467,8 @@ def main():
                    "layout": args.layout, "shard": [b, e], "shard_elems": S,
                    "world": w.world, "rank": w.rank, "tensors": len(w.tensors),
                    "grad_pool": len(pool), "bytes_per_param_step": upd_bytes + NORM_BYTES,
-                   "update": variant, "launch": "graph" if args.graph else "stream"},
+                   "update": variant, "launch": "graph" if args.graph else "stream",
+                   "placement": args.placement, "arena_bytes": arrays["arena_bytes"]},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": f"adamwTileKernel<{variant}{',scheduled' if args.graph else ''}>",

@@ -38,7 +38,7 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
            "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
            "bfo_stream_mix", "bfo_plan_runs", "bfo_step_scalars_fill", "adamw_sr_step_scheduled",
-           "bfo_cursor_advance")
+           "bfo_cursor_advance", "bfo_spread_layout")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -125,6 +125,7 @@ def _lib():
         "adamw_sr_step_scheduled": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, u64, vp, vp,
                                           vp, i32, vp]),
         "bfo_cursor_advance": (i32, [vp, vp]),
+        "bfo_spread_layout": (i32, [pu64, u32, pu64, pu64]),
         "bfo_status_string": (ctypes.c_char_p, [i32]),
         "bfo_last_hip_error": (i32, []),
     }
@@ -384,6 +385,20 @@ def cursor_advance(cursor):
     c = _arg(cursor, torch.int64, 1, "cursor", cursor.device)
     with torch.cuda.device(cursor.device):
         _check("bfo_cursor_advance", _lib().bfo_cursor_advance(c, _stream(cursor.device)))
+
+
+REGION_BYTES = 1 << 34
+
+
+def spread_layout(sizes):
+    """(offsets, total) placing arrays of `sizes` bytes each on its own 16 GiB
+    boundary after the previous (bfo_spread_layout)."""
+    n = len(sizes)
+    b = (ctypes.c_uint64 * max(1, n))(*sizes)
+    off = (ctypes.c_uint64 * max(1, n))()
+    tot = ctypes.c_uint64(0)
+    _check("bfo_spread_layout", _lib().bfo_spread_layout(b, n, off, ctypes.byref(tot)))
+    return list(off[:n]), tot.value
 
 
 def lr_at(kind, step, warmup_steps, total_steps, lr_max, final_frac=0.0, decay_frac=0.0):

@@ -485,6 +485,23 @@ int bfo_stream_mix(uint16_t *params, const uint16_t *grads, float *master, float
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
+int bfo_spread_layout(const uint64_t *bytes, uint32_t count, uint64_t *offsets, uint64_t *total) {
+    if (!total || (count && (!bytes || !offsets))) return BFO_EINVAL;
+    uint64_t end = 0;
+    for (uint32_t k = 0; k < count; ++k) {
+        uint64_t start = 0;
+        if (k) {
+            if (end > UINT64_MAX - (BFO_REGION_BYTES - 1)) return BFO_ERANGE;
+            start = (end + BFO_REGION_BYTES - 1) / BFO_REGION_BYTES * BFO_REGION_BYTES;
+        }
+        if (bytes[k] > UINT64_MAX - start) return BFO_ERANGE;
+        offsets[k] = start;
+        end = start + bytes[k];
+    }
+    *total = end;
+    return BFO_OK;
+}
+
 const char *bfo_status_string(int status) {
     switch (status) {
         case BFO_OK: return "ok";

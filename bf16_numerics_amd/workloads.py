@@ -176,6 +176,26 @@ def init_state(torch, w: Workload, begin: int, end: int, device, seed=SEED, mast
     return P, M, m, v
 
 
+def init_params_into(torch, w: Workload, begin: int, P, M=None, seed=SEED, chunk=1 << 27):
+    """Initial bf16 params for global [begin, begin + len(P)) written into the
+    existing tensor P (and their fp32 copy into M), chunk by chunk, so that no
+    full-size temporary is needed.  Same distribution as init_state; each
+    chunk has its own seeded generator."""
+    count = P.numel()
+    for c0 in range(0, count, chunk):
+        c1 = min(count, c0 + chunk)
+        g = _gen(torch, P.device, (seed * 1000003 + begin + c0) % (1 << 62))
+        tmp = torch.empty(c1 - c0, dtype=torch.float32, device=P.device)
+        if w.param_kind == "uniform":
+            tmp.uniform_(w.param_range[0], w.param_range[1], generator=g)
+        else:
+            tmp.normal_(0.0, w.param_std, generator=g)
+        P[c0:c1] = tmp.to(torch.bfloat16)
+        if M is not None:
+            M[c0:c1] = P[c0:c1].to(torch.float32)
+    return P
+
+
 def fill_grads(torch, w: Workload, G, begin: int, step: int, seed=SEED, stds=None):
     """Write step `step`'s bf16 grads for global [begin, begin + len(G)) into G."""
     end = begin + G.numel()

@@ -179,3 +179,25 @@ def test_checkpoint_latest_reads_done_markers(bfo, tmp_path):
     assert lib.bfo_checkpoint_done(None, 1) == bfo.EINVAL
     assert lib.bfo_checkpoint_save(b"/tmp", None, None, None, None, None, 1, 1, None) == bfo.EINVAL
     assert lib.bfo_checkpoint_load(b"/tmp", 1, None, None, None, None, None, None, None) == bfo.EINVAL
+
+
+def test_spread_layout_puts_each_array_on_its_own_16_gib_boundary(bfo):
+    R = 1 << 34
+    sizes = [3_115_372_800, 4 * 389_421_600, 778_843_200, 778_843_200, 778_843_200]
+    offsets, total = bfo.spread_layout(sizes)
+    assert offsets == [0, R, 2 * R, 3 * R, 4 * R] and total == 4 * R + sizes[-1]
+    # arrays larger than a region take as many whole regions as they need
+    offsets, total = bfo.spread_layout([R + 1, 5, R])
+    assert offsets == [0, 2 * R, 3 * R] and total == 4 * R
+    # at every element index, arrays of non-decreasing element size stay a region or more apart
+    for a, b in zip(offsets, offsets[1:]):
+        assert b - a >= R
+    assert bfo.spread_layout([]) == ([], 0)
+    assert bfo.spread_layout([0, 0]) == ([0, 0], 0)
+    lib = bfo.library()
+    tot = ctypes.c_uint64()
+    big = (ctypes.c_uint64 * 2)(2 ** 64 - R + 5, 8)       # the second start would pass 2^64
+    off = (ctypes.c_uint64 * 2)()
+    assert lib.bfo_spread_layout(big, 2, off, ctypes.byref(tot)) == bfo.ERANGE
+    assert lib.bfo_spread_layout(None, 1, off, ctypes.byref(tot)) == bfo.EINVAL
+    assert lib.bfo_spread_layout(big, 1, off, None) == bfo.EINVAL

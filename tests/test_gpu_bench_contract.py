@@ -31,6 +31,7 @@ def test_bench_line_follows_the_contract():
     assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
     assert d["unit"] == "Gparams/s" and d["higher_is_better"] is True and d["data"] == "synthetic"
     assert d["config"]["workload"] == "tiny_gpt_d32" and d["config"]["launch"] == "stream"
+    assert d["config"]["placement"] == "spread" and d["config"]["arena_bytes"] > 0
     assert abs(d["value"] - d["config"]["shard_elems"] / (d["ms_per_step"] * 1e-3) / 1e9) <= 1e-3 * d["value"] + 1e-3
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
