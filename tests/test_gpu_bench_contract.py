@@ -52,6 +52,13 @@ def test_bench_graph_mode_line():
     assert d["value"] > 0 and d["ms_per_step"] > 0 and "cpu_baseline" not in d
 
 
+def test_bench_packed_placement_line():
+    d = run_bench("--workload", "tiny_gpt_d32", "--steps", "10", "--warmup", "2", "--no-cpu-baseline",
+                  "--placement", "packed")
+    assert d["config"]["placement"] == "packed" and d["config"]["arena_bytes"] == 0
+    assert d["roofline"]["traffic"] is None and d["value"] > 0
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"], capture_output=True,
                        text=True, timeout=60, cwd=ROOT)
