@@ -502,7 +502,11 @@ def main():
     if not args.no_cpu_baseline and args.layout == "flat":
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
         out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds, args.rounding == "sr")
-    if not args.no_ceiling:
+    if not args.no_ceiling and (P.data_ptr() % 16 or pool[0].data_ptr() % 16):
+        # the streaming kernel moves 16-byte vectors only
+        out["ceiling"] = {"skipped": "params or grads not 16-byte aligned (the update takes its per-element "
+                                     "path for them)"}
+    elif not args.no_ceiling:
         out["ceiling"] = stream_ceiling(
             torch, bfo, stream, P[:S], pool[0][:S], M, m, v, args.steps, achieved,
             norm=lambda k: bfo.grad_global_norm(T, pool[k % len(pool)], res, w.hparams.max_norm),
