@@ -491,8 +491,10 @@ int bfo_spread_layout(const uint64_t *bytes, uint32_t count, uint64_t *offsets, 
     for (uint32_t k = 0; k < count; ++k) {
         uint64_t start = 0;
         if (k) {
-            if (end > UINT64_MAX - (BFO_REGION_BYTES - 1)) return BFO_ERANGE;
+            if (end > UINT64_MAX - 2 * BFO_REGION_BYTES) return BFO_ERANGE;
             start = (end + BFO_REGION_BYTES - 1) / BFO_REGION_BYTES * BFO_REGION_BYTES;
+            // the fourth region of every 64 GiB-aligned block starts no array
+            if ((start / BFO_REGION_BYTES) % 4 == 3) start += BFO_REGION_BYTES;
         }
         if (bytes[k] > UINT64_MAX - start) return BFO_ERANGE;
         offsets[k] = start;

@@ -390,11 +390,17 @@ int bfo_checkpoint_load(const char *dir, uint64_t step, bfo_table table, uint16_
  * physical backing then follows its virtual layout) at the offsets below,
  * and fill the gaps with its other buffers.  Placement changes no result.
  *
+ * Which regions also matters, a little for five arrays and a lot for four:
+ * four arrays in the four regions of one 64 GiB-aligned block run at the
+ * lower rate again, so the layout below starts no array in the fourth
+ * region of a block.
+ *
  * bfo_spread_layout: for `count` arrays of bytes[k] bytes (in that order),
  * offsets[k] = the first multiple of BFO_REGION_BYTES at or after the end
- * of array k-1 (offsets[0] = 0), *total = offsets[count-1] + bytes[count-1]
- * (0 when count is 0).  BFO_EINVAL for null pointers with count > 0 and
- * BFO_ERANGE if the total does not fit in 64 bits.  Host only. */
+ * of array k-1 that is not the fourth region of a 64 GiB-aligned block
+ * (offsets[0] = 0); *total = offsets[count-1] + bytes[count-1] (0 when
+ * count is 0).  BFO_EINVAL for null pointers with count > 0 and BFO_ERANGE
+ * if an offset or the total does not fit in 64 bits.  Host only. */
 #define BFO_REGION_BYTES (1ull << 34)
 int bfo_spread_layout(const uint64_t *bytes, uint32_t count, uint64_t *offsets, uint64_t *total);
 

@@ -185,10 +185,12 @@ def test_spread_layout_puts_each_array_on_its_own_16_gib_boundary(bfo):
     R = 1 << 34
     sizes = [3_115_372_800, 4 * 389_421_600, 778_843_200, 778_843_200, 778_843_200]
     offsets, total = bfo.spread_layout(sizes)
-    assert offsets == [0, R, 2 * R, 3 * R, 4 * R] and total == 4 * R + sizes[-1]
+    assert offsets == [0, R, 2 * R, 4 * R, 5 * R] and total == 5 * R + sizes[-1]   # region 3 is skipped
     # arrays larger than a region take as many whole regions as they need
     offsets, total = bfo.spread_layout([R + 1, 5, R])
-    assert offsets == [0, 2 * R, 3 * R] and total == 4 * R
+    assert offsets == [0, 2 * R, 4 * R] and total == 5 * R
+    offsets, _ = bfo.spread_layout([1] * 8)
+    assert offsets == [r * R for r in (0, 1, 2, 4, 5, 6, 8, 9)]
     # at every element index, arrays of non-decreasing element size stay a region or more apart
     for a, b in zip(offsets, offsets[1:]):
         assert b - a >= R
