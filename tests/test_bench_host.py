@@ -1,6 +1,7 @@
 """Host-side checks of bench.py (no GPU): the one-GPU guard, the CPU oracle
 baseline leg and the rule that counter traffic is reported only for the
 kernel source it was measured on."""
+import glob
 import json
 import os
 import subprocess
@@ -59,3 +60,27 @@ def test_counter_traffic_is_reported_only_for_the_measured_source(tmp_path, monk
     (prof / "adamw_update_wl_traffic.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("wl") is None
     assert bench.measured_traffic("missing") is None
+
+
+@pytest.mark.parametrize("path", sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))))
+def test_committed_counter_records_are_consistent(path):
+    """Each stored counter record adds up: read + write bytes, 28 B per shard
+    element for the update, counter bytes within 1% above the algorithmic
+    ones, and the copy calibration it was scaled by."""
+    rec = json.load(open(path))
+    w = W.WORKLOADS[rec["workload"]]()
+    begin, end = w.shard()
+    assert rec["shard_elems"] == end - begin
+    assert rec["algorithmic_bytes_per_launch"] == 28 * rec["shard_elems"]
+    assert rec["bytes_per_launch"] == pytest.approx(rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"],
+                                                    abs=2)
+    ratio = rec["bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+    assert rec["traffic_over_algorithmic"] == pytest.approx(ratio, abs=1e-5)
+    assert 1.0 <= ratio < 1.01
+    cal = rec["copy_reference"]
+    assert rec["fetch_scale"] == pytest.approx(cal["read_KiB"] / np.mean(cal["FETCH_SIZE_KiB"]), rel=1e-5)
+    assert rec["write_scale"] == pytest.approx(cal["write_KiB"] / np.mean(cal["WRITE_SIZE_KiB"]), rel=1e-5)
+    assert rec["read_bytes_per_launch"] == pytest.approx(
+        np.mean(rec["update_FETCH_SIZE_KiB"]) * 1024 * rec["fetch_scale"], rel=1e-6)
+    assert rec["write_bytes_per_launch"] == pytest.approx(
+        np.mean(rec["update_WRITE_SIZE_KiB"]) * 1024 * rec["write_scale"], rel=1e-6)
