@@ -574,6 +574,51 @@ def test_full_size_gpt2_1p5b_shard_variants(bfo, master, rounding):
     print(f"gpt2_1p5b rank {w.rank} master={master} rounding={rounding}: scale {got[2]:.6f}", flush=True)
 
 
+def test_full_size_gpt2_1p5b_shard_in_the_benchmark_placement(bfo):
+    # The benchmark's own arrays: params, a two-buffer grads pool, master, m
+    # and v carved from one arena of most of device memory, each on its own
+    # 16 GiB region (bench.state_arrays, spread placement), the launches
+    # bench.py times; two steps, sampled windows against the oracle.
+    import bench
+    w = W.gpt2_1p5b_shard()
+    ents = w.entries()
+    T = bfo.Table(ents, w.world, w.rank)
+    b, e = T.begin, T.end
+    S = e - b
+    g_stride = (S + 127) // 128 * 128
+    arrays = bench.state_arrays(torch, bfo, torch.device(DEV), "spread", w.n, g_stride, 2, S, True,
+                                (16 << 30) + S * 6)
+    P_full, pool_mem, M, m, v = (arrays[k] for k in ("P", "G", "M", "m", "v"))
+    assert arrays["arena_bytes"] > 0
+    P_full.view(torch.int16).fill_(0x7FA5)                                 # sentinel NaN pattern
+    P = P_full[b:e]
+    W.init_params_into(torch, w, b, P, M)
+    m.zero_()
+    v.zero_()
+    pool = [pool_mem[k * g_stride:k * g_stride + S] for k in range(2)]
+    st = {"P": P, "M": M, "m": m, "v": v}
+    res = bfo.new_norm_result(DEV)
+    tbl = o.table(ents)
+    wins = windows(ents, b, e, seed=11)
+    for t in (1, 2):
+        G = pool[t - 1]
+        W.fill_grads(torch, w, G, b, t)
+        st["G"] = G
+        pre = [host_copy(st, lo - b, hi - b) for lo, hi in wins]
+        bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
+        bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, t, step_seed(t), scale=res)
+        got_norm = bfo.read_norm_result(res)
+        Gh = G.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert_norm_parity(got_norm, o.grad_norm(Gh, w.hparams.max_norm))
+        del Gh
+        for (lo, hi), h in zip(wins, pre):
+            oracle_step(tbl, lo, h, w.hparams, got_norm[2], t, step_seed(t), o.ROUND_SR)
+            assert_state_parity(host_copy(st, lo - b, hi - b), h, f"spread [{lo},{hi}) t={t}")
+    outside = torch.cat([P_full[:b], P_full[e:]]).view(torch.int16)
+    assert bool((outside == 0x7FA5).all()), "a write escaped the shard"
+    del arrays, P_full, pool_mem, M, m, v, P, pool, st
+
+
 def test_full_size_rebuild_gpt2_1p5b_shard(bfo):
     # The resume rebuild at the benchmark's size and shard: after a step, the
     # master and that step's seed give back the step's bf16 params bit for
