@@ -306,6 +306,38 @@ def test_update_is_deterministic(bfo):
         assert np.array_equal(outs[0][1][k].view(np.uint8), outs[1][1][k].view(np.uint8)), k
 
 
+@pytest.mark.parametrize("rounding", [o.ROUND_SR, o.ROUND_RNE])
+def test_master_path_never_reads_the_params(bfo, rounding):
+    # With a master the update takes the old weight from the master and only
+    # writes the bf16 params (which is why their stores may bypass the
+    # caches): params holding NaN patterns before the step give the same
+    # bits as the real params, on a whole buffer and on a rank whose params
+    # and grads are views into full-length buffers starting mid-line.
+    w = ragged_workload(40, 12)                        # n = 163,852: 4 shards of 40,963 (odd)
+    for world, rank in ((1, 0), (4, 1)):
+        T = bfo.Table(w.entries(), world, rank)
+        b, e = T.begin, T.end
+        st = device_state(w, b, e, DEV)
+        W.fill_grads(torch, w, st["G"], b, 1)
+        outs = []
+        for poison in (False, True):
+            P_full = torch.zeros(w.n, dtype=torch.bfloat16, device=DEV)
+            G_full = torch.zeros(w.n, dtype=torch.bfloat16, device=DEV)
+            P, G = P_full[b:e], G_full[b:e]
+            P.copy_(st["P"])
+            G.copy_(st["G"])
+            if poison:
+                P.view(torch.int16).fill_(0x7FC1)
+            s2 = {"P": P, "G": G, "M": st["M"].clone(), "m": st["m"].clone(), "v": st["v"].clone()}
+            res = bfo.new_norm_result(DEV)
+            bfo.grad_global_norm(T, G, res)
+            bfo.adamw_sr_step(T, P, G, s2["M"], s2["m"], s2["v"], w.hparams, 1, step_seed(1), scale=res,
+                              rounding=rounding)
+            outs.append(host_copy(s2))
+        for k in ("P", "M", "m", "v"):
+            assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), (world, rank, k)
+
+
 def test_shard_concatenation_bit_identical(bfo):
     # Running each 1/N shard separately rebuilds the unsharded result bit for
     # bit (the draws are keyed on the global index), with the global clip scale.
