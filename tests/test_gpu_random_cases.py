@@ -20,7 +20,7 @@ from bf16_numerics_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-CASES = 48
+CASES = 256
 
 
 @pytest.fixture(scope="module")
