@@ -130,7 +130,8 @@ __device__ __forceinline__ uint4 load8Narrow(const uint16_t *p) {
 // after an update, the norm's read of the next grads no longer has to drain
 // the update's write-back as it goes (in-step norm on the 1.5B shard 109 ->
 // 66 us), and the whole step ran 2.5% faster although that write-back now
-// lands in the update.  Arrays that are read and then written back (m, v,
+// lands in the update (3% also when fresh grads are written before every
+// step, as a backward pass would).  Arrays that are read and then written back (m, v,
 // master, the no-master params) keep plain loads: nontemporal ones slowed
 // that mix by 3-8%.
 typedef unsigned int U32x4v __attribute__((ext_vector_type(4)));
@@ -146,7 +147,8 @@ __device__ __forceinline__ uint4 loadOnce16(const uint16_t *p, uint64_t vec) {
 // faster on the 1.5B shard's rank 1 (its params start 32 bytes into a line)
 // and 0.2-0.4% on line-aligned shards.  Without a master the params are read
 // and written back, and nontemporal stores cost 1.1% there; nontemporal
-// stores of m, v and the master gained nothing.
+// stores of m, v and the master gained nothing.  The rebuild, which only
+// writes the params too, gained 4-5% from them.
 __device__ __forceinline__ void storeOnce16(uint16_t *p, uint64_t vec, const uint4 &x) {
     __builtin_nontemporal_store(U32x4v{x.x, x.y, x.z, x.w}, reinterpret_cast<U32x4v *>(p) + vec);
 }
@@ -669,9 +671,10 @@ __global__ __launch_bounds__(kBlock) void normStage1FlatKernel(const uint16_t *_
 }
 
 // Workgroups take tiles from the shard's end backwards: the partial of a tile
-// depends only on its index, so the order changes no bit of the result, and the
-// lines read last (the shard's start) are the ones the update, which walks
-// forward, reads first while they may still sit in the memory-side cache.
+// depends only on its index, so the order changes no bit of the result.  The
+// order was chosen for plain loads, whose last lines (the shard's start) the
+// update, walking forward, could still find in the memory-side cache; with
+// nontemporal loads forward and backward measured the same.
 __global__ __launch_bounds__(kBlock) void normStage1Kernel(const uint16_t *__restrict__ G, uint64_t S,
                                                            ShardView sv, int pgVec,
                                                            double *__restrict__ partials, uint64_t tileBase,
