@@ -26,6 +26,7 @@ UPDATE_BYTES = 28              # G 2 + m 4+4 + v 4+4 + M 4+4 + P 2 per parameter
 UPDATE_BYTES_NO_MASTER = 22    # G 2 + P 2+2 + m 4+4 + v 4+4
 NORM_BYTES = 2                 # G read once
 REBUILD_BYTES = 6              # master_to_bf16_sr: M 4 read + P 2 written
+TARGET_FRAC = 0.80             # the bar set for the step's kernels: 80% of HBM peak
 METRIC = "optimizer Gparams/s per step + achieved HBM GB/s (% of peak), 1 MI355X"
 WORKLOAD_NAMES = ("tiny_gpt_d32", "gpt2_124m", "gpt2_1p5b_shard", "stall16m", "llama7b")
 
@@ -50,6 +51,18 @@ def measured_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_threads():
     """Host threads this process may use (the CPU share, not the machine)."""
     k = len(os.sched_getaffinity(0))
@@ -65,7 +78,6 @@ def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
     before the clip scale).  The oracle's C functions run without the GIL."""
     from concurrent.futures import ThreadPoolExecutor
 
-    import numpy as np
     import oracle as o
     from bf16_numerics_amd import workloads as W
 
@@ -85,8 +97,7 @@ def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
             steps += 1
             t = first_step + steps
             sums = list(pool.map(lambda r: o.grad_norm(h["G"][r[0]:r[1]], max_norm)[0], parts))
-            norm = float(np.float32(np.sqrt(sum(sums))))
-            scale = float(np.float32(max_norm / norm)) if norm > max_norm else 1.0
+            _, scale = o.norm_from_sumsq(sum(sums), max_norm)
             list(pool.map(lambda r: o.adamw_step(tbl, begin + r[0], h["P"][r[0]:r[1]], h["G"][r[0]:r[1]],
                                                  sl(h["M"], r), h["m"][r[0]:r[1]], h["v"][r[0]:r[1]], hp,
                                                  scale, t, (1337 << 32) | t, rounding), parts))
@@ -102,6 +113,7 @@ def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
         sk, elk = run(list(zip(cuts[:-1], cuts[1:])), pool, target_s / 2, s1)
     one = count * s1 / el1 / 1e9
     return {"value": count * sk / elk / 1e9, "unit": "Gparams/s", "cores": k, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"contiguous {count}-element slice of the {w.name} shard, grad norm + AdamW update "
                       f"({'master' if h['M'] is not None else 'no master'}, {'SR' if rounding_sr else 'RNE'}) "
                       f"per step: {sk} steps in {elk:.1f} s on {k} threads (static contiguous partition); "
@@ -238,8 +250,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2_1p5b_shard",
-                    choices=WORKLOAD_NAMES)
+    ap.add_argument("--workload", default="llama7b", choices=WORKLOAD_NAMES,
+                    help="llama7b (default: the largest configuration that fits one GPU, 6.74e9 parameters "
+                         "in one shard), gpt2_1p5b_shard (rank 1 of 8 of the 1.5B model), gpt2_124m, "
+                         "stall16m, tiny_gpt_d32")
     ap.add_argument("--grad-pool", type=int, default=4)
     ap.add_argument("--layout", choices=("flat", "per_tensor"), default="flat",
                     help="ZeRO-1 shard layout: contiguous range, or 1/N of every tensor")
@@ -474,6 +488,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": f"adamwTileKernel<{variant}{',scheduled' if args.graph else ''}>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "target_frac": TARGET_FRAC,
+                     "shortfall_vs_target": round(TARGET_FRAC - achieved / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": upd_bytes * S,
                      "update_ms_avg": round(upd_avg, 5), "update_ms_median": round(upd_median, 5)},
         "step_ms_events": {"mean": round(sum(step_ev_ms) / len(step_ev_ms), 5),

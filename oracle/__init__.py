@@ -62,6 +62,7 @@ def _load():
         "oracle_table_check": (ctypes.c_int, [_vp, ctypes.c_uint32, _u64p]),
         "oracle_decay_mask": (ctypes.c_int, [_vp, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64, _vp]),
         "oracle_grad_norm": (None, [_vp, ctypes.c_uint64, ctypes.c_float, _f64p, _f32p, _f32p]),
+        "oracle_norm_from_sumsq": (None, [ctypes.c_double, ctypes.c_float, _f32p, _f32p]),
         "oracle_bias_corrections": (None, [ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.c_int, _f32p, _f32p]),
         "oracle_adamw_step": (ctypes.c_int, [_vp, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64,
                                              _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_HParams),
@@ -175,6 +176,14 @@ def grad_norm(g, max_norm=1.0):
     sc = ctypes.c_float(0.0)
     _load().oracle_grad_norm(_ptr(g), g.size, max_norm, ctypes.byref(s), ctypes.byref(nrm), ctypes.byref(sc))
     return s.value, nrm.value, sc.value
+
+
+def norm_from_sumsq(sumsq, max_norm=1.0):
+    """(norm, scale) for a sum of squares formed elsewhere."""
+    nrm = ctypes.c_float(0.0)
+    sc = ctypes.c_float(0.0)
+    _load().oracle_norm_from_sumsq(sumsq, max_norm, ctypes.byref(nrm), ctypes.byref(sc))
+    return nrm.value, sc.value
 
 
 def bias_corrections(beta1, beta2, t, bias_correction=True):

@@ -245,7 +245,15 @@ int oracle_decay_mask(const oracle_tensor *t, uint32_t ntensors, uint64_t begin,
  * sum of squares of the widened bf16 values in binary64, added in ascending
  * index order (every bf16 square is exact in binary64); norm is its square
  * root rounded to binary32; scale is max_norm / norm when norm exceeds
- * max_norm, else 1 (for max_norm = 1 this is min(1, 1/norm)). */
+ * max_norm, else 1 (for max_norm = 1 this is min(1, 1/norm)).
+ * oracle_norm_from_sumsq is that last part alone, for a sum of squares
+ * added up elsewhere (e.g. the shards' parts, added before the root). */
+void oracle_norm_from_sumsq(double sumsq, float max_norm, float *norm, float *scale) {
+    float nrm = (float)sqrt(sumsq);
+    *norm = nrm;
+    *scale = (nrm > max_norm) ? max_norm / nrm : 1.0f;
+}
+
 void oracle_grad_norm(const uint16_t *g, uint64_t count, float max_norm,
                       double *sumsq, float *norm, float *scale) {
     double s = 0.0;
@@ -253,10 +261,8 @@ void oracle_grad_norm(const uint16_t *g, uint64_t count, float max_norm,
         double x = (double)oracle_bf16_to_f32(g[j]);
         s += x * x;
     }
-    float nrm = (float)sqrt(s);
     *sumsq = s;
-    *norm = nrm;
-    *scale = (nrm > max_norm) ? max_norm / nrm : 1.0f;
+    oracle_norm_from_sumsq(s, max_norm, norm, scale);
 }
 
 /* ------------------------------------------------------------------ */

@@ -281,6 +281,26 @@ def test_norm_brute_force_exact_and_extremes():
     assert o.grad_norm(np.array([0x3F80], np.uint16), 1.0)[2] == 1.0
 
 
+def test_norm_from_sumsq_closed_forms():
+    # The root and the clip scale alone: sum of squares 16 -> norm 4, scale
+    # 1/4 (max 1) or 1/2 (max 2); 1/4 -> 1/2, not clipped; a norm equal to
+    # the maximum is not clipped; an infinite sum -> scale 0; the root is
+    # rounded once to binary32 (sum 2 -> fp32(sqrt 2)).
+    assert o.norm_from_sumsq(16.0, 1.0) == (4.0, 0.25)
+    assert o.norm_from_sumsq(16.0, 2.0) == (4.0, 0.5)
+    assert o.norm_from_sumsq(0.25, 1.0) == (0.5, 1.0)
+    assert o.norm_from_sumsq(1.0, 1.0) == (1.0, 1.0)
+    assert o.norm_from_sumsq(0.0, 1.0) == (0.0, 1.0)
+    assert o.norm_from_sumsq(math.inf, 1.0) == (math.inf, 0.0)
+    norm, scale = o.norm_from_sumsq(2.0, 1.0)
+    assert norm == np.float32(math.sqrt(2.0)) and scale == np.float32(1.0) / np.float32(math.sqrt(2.0))
+    # parts added before the root give the whole buffer's norm (exact here: every
+    # square and partial sum of these patterns is representable)
+    g = np.full(1 << 20, 0x3A80, np.uint16)               # 2^-10: sum 2^-20 per element
+    halves = o.grad_norm(g[: 1 << 19], 1.0)[0] + o.grad_norm(g[1 << 19:], 1.0)[0]
+    assert halves == 1.0 and o.norm_from_sumsq(halves, 0.5) == (1.0, 0.5)
+
+
 # ---------------------------------------------------------------- update
 
 
