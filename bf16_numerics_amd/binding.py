@@ -38,7 +38,7 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
            "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
            "bfo_stream_mix", "bfo_plan_runs", "bfo_step_scalars_fill", "adamw_sr_step_scheduled",
-           "bfo_cursor_advance", "bfo_spread_layout")
+           "bfo_cursor_advance", "bfo_spread_layout", "bfo_norm_workspace_bytes")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -103,7 +103,8 @@ def _lib():
         "bfo_table_runs": (i32, [vp, ctypes.POINTER(BfoRun), u32, ctypes.POINTER(u32)]),
         "bfo_table_destroy": (i32, [vp]),
         "bfo_table_info": (i32, [vp, pu64, pu64, pu64]),
-        "grad_global_norm": (i32, [vp, vp, ctypes.c_float, vp, vp]),
+        "grad_global_norm": (i32, [vp, vp, ctypes.c_float, vp, vp, vp]),
+        "bfo_norm_workspace_bytes": (i32, [vp, pu64]),
         "adamw_sr_step": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, vp, u64, u64, i32, vp]),
         "bfo_lr_at": (i32, [ctypes.POINTER(LrSchedule), u64, ctypes.POINTER(ctypes.c_float)]),
         "bfo_outlier_create": (i32, [u32, ctypes.c_float, ctypes.POINTER(vp)]),
@@ -290,13 +291,32 @@ def scale_ptr(res):
     return res.data_ptr() + 12
 
 
-def grad_global_norm(table, grads, out, max_norm=1.0):
+def norm_workspace_bytes(table):
+    """Device bytes grad_global_norm needs as workspace for this table."""
+    out = ctypes.c_uint64(0)
+    _check("bfo_norm_workspace_bytes", _lib().bfo_norm_workspace_bytes(table.handle, ctypes.byref(out)))
+    return out.value
+
+
+def new_norm_workspace(table):
+    """A device buffer of norm_workspace_bytes(table) bytes (at least 8)."""
+    return torch.empty(max(8, norm_workspace_bytes(table)), dtype=torch.uint8, device=table.device)
+
+
+def grad_global_norm(table, grads, out, max_norm=1.0, workspace=None):
+    """workspace: new_norm_workspace(table), or None for the table's own buffer."""
     dev = table.device
     g = _arg(grads, torch.bfloat16, table.pg_size, "grads", dev)
     if out.dtype != torch.float64 or out.numel() != 2 or out.device != dev:
         raise ValueError("out must be new_norm_result(device)")
+    ws = None
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous() or \
+                workspace.numel() * workspace.element_size() < norm_workspace_bytes(table):
+            raise ValueError("workspace must be new_norm_workspace(table)")
+        ws = ctypes.c_void_p(workspace.data_ptr())
     with torch.cuda.device(dev):
-        _check("grad_global_norm", _lib().grad_global_norm(table.handle, g, max_norm,
+        _check("grad_global_norm", _lib().grad_global_norm(table.handle, g, max_norm, ws,
                                                            ctypes.c_void_p(out.data_ptr()), _stream(dev)))
     return out
 

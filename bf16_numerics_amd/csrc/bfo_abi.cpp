@@ -384,16 +384,27 @@ int launchStep(bfo_table table, uint16_t *params, const uint16_t *grads, float *
 
 extern "C" {
 
-int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
-                     void *stream) {
+int bfo_norm_workspace_bytes(bfo_table table, uint64_t *bytes) {
+    if (!table || !bytes) return BFO_EINVAL;
+    *bytes = bfo::normWorkspaceBytes(table->S);
+    return BFO_OK;
+}
+
+int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, void *workspace,
+                     bfo_norm_result *out, void *stream) {
     if (!table || !out || (table->S && !grads)) return BFO_EINVAL;
-    if (!alignedTo(grads, 2) || !alignedTo(out, 16)) return BFO_EMISALIGNED;
-    if (anyOverlap({span(grads, 2 * pgElems(table)), span(out, sizeof(bfo_norm_result))})) return BFO_EINVAL;
+    if (!(max_norm > 0.0f)) return BFO_EINVAL;                // also refuses NaN; +inf disables the clip
+    if (!alignedTo(grads, 2) || !alignedTo(out, 16) || !alignedTo(workspace, 8)) return BFO_EMISALIGNED;
+    const uint64_t wsBytes = bfo::normWorkspaceBytes(table->S);
+    if (anyOverlap({span(grads, 2 * pgElems(table)), span(out, sizeof(bfo_norm_result)),
+                    span(workspace, wsBytes)}))
+        return BFO_EINVAL;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
+    double *partials = workspace ? static_cast<double *>(workspace) : table->normPartials;
     hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0,
-                                    table->layout == BFO_LAYOUT_FLAT, max_norm,
-                                    table->normPartials, out, static_cast<hipStream_t>(stream));
+                                    table->layout == BFO_LAYOUT_FLAT, max_norm, partials, out,
+                                    static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 

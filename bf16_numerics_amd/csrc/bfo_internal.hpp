@@ -39,6 +39,12 @@ inline uint64_t normTiles(uint64_t S) { return ((S + 7) / 8 + kNormTileVecs - 1)
 inline uint64_t normRuns(uint64_t ntiles) {
     return ntiles > kNormFinishDirect ? (ntiles + kNormReduceRun - 1) / kNormReduceRun : 0;
 }
+// Device bytes of binary64 partials the norm of an S-element shard writes
+// and reads back (none when one workgroup does all of it).
+inline uint64_t normWorkspaceBytes(uint64_t S) {
+    const uint64_t t = normTiles(S);
+    return t <= kNormSmallTiles ? 0 : (t + normRuns(t)) * sizeof(double);
+}
 
 // Device view of a table's shard plan.  A run is a stretch of shard-local
 // elements [local[k], local[k+1]) that sits at consecutive positions of the

@@ -51,15 +51,16 @@
  *     bfo_status_string() names it.  BFO_EHIP means a HIP runtime call
  *     failed; bfo_last_hip_error() gives its hipError_t code for the calling
  *     thread.  The library never prints and never exits.
- *   - Concurrency.  A table may be used from several threads, but calls on
- *     one table whose GPU work overlaps in time (different streams without
- *     ordering) race on the table's norm workspace.
+ *   - Concurrency.  A table may be used from several threads and streams;
+ *     the one shared buffer is the norm workspace a table holds for callers
+ *     that pass none (see grad_global_norm).
  *
  * A step, as a ZeRO-1 rank runs it (error checks left out):
  *   bfo_table tb;  bfo_table_create(tensors, count, world, rank, &tb);   once
  *   bfo_norm_result *res;  (16-byte aligned device memory)              once
+ *   void *workspace;  (bfo_norm_workspace_bytes(tb) bytes of device memory) once
  *   per step t = 1, 2, ...:
- *     grad_global_norm(tb, grads + begin, 1.0f, res, stream);
+ *     grad_global_norm(tb, grads + begin, 1.0f, workspace, res, stream);
  *     adamw_sr_step(tb, params + begin, grads + begin, master, m, v, &hp,
  *                   &res->scale, NULL, t, seed_t, BFO_ROUND_SR, stream);
  *   (the all-gather of params and the reduce-scatter of grads around it are
@@ -189,6 +190,12 @@ int bfo_table_runs(bfo_table table, bfo_run *out, uint32_t capacity, uint32_t *c
 int bfo_plan_runs(const bfo_tensor *tensors, uint32_t count, uint32_t world, uint32_t rank, int layout,
                   bfo_run *out, uint32_t capacity, uint32_t *nruns, uint64_t *shard_elems);
 
+/* *bytes = the device workspace grad_global_norm needs for this table: one
+ * binary64 partial per 8,192-element tile of the shard, plus one per 4,096
+ * tiles above 32,768 tiles; 0 for shards of at most 8 tiles (65,536
+ * elements), whose norm runs in one workgroup.  Host only. */
+int bfo_norm_workspace_bytes(bfo_table table, uint64_t *bytes);
+
 /* Deterministic global grad norm of one shard ("04 · 多 GPU 与混合精度" §4:
  * grad_norm, then grad_scale = min(1, 1/grad_norm), i.e. clip to 1.0; under
  * ZeRO-1 this is the shard's part, which ranks would add before the root).
@@ -197,9 +204,16 @@ int bfo_plan_runs(const bfo_tensor *tensors, uint32_t count, uint32_t world, uin
  * depends only on the shard length, so repeated calls give identical bits.
  * scale = max_norm / norm when norm > max_norm, else 1.0f (an infinite norm
  * gives 0, a NaN norm gives 1: non-finite grads are not sanitised, check
- * norm).  An empty shard gives {0, 0, 1}. */
-int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
-                     void *stream);
+ * norm).  An empty shard gives {0, 0, 1}.  max_norm must be > 0 (+inf
+ * turns clipping off); zero, negative or NaN -> BFO_EINVAL.
+ * workspace: device memory of at least bfo_norm_workspace_bytes bytes,
+ * 8-byte aligned, owned by the caller, written and read by this call only
+ * (its contents before and after mean nothing); calls with separate
+ * workspaces may run at the same time on different streams.  NULL uses a
+ * buffer the table holds, so calls on one table with a NULL workspace must
+ * not overlap in time. */
+int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, void *workspace,
+                     bfo_norm_result *out, void *stream);
 
 /* One AdamW step over the shard ("04 · 多 GPU 与混合精度" §2.2, with the
  * lerp computed as two fused multiply-adds; "第 13 讲" §1.7 for bias

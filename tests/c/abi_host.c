@@ -46,7 +46,7 @@ int main(int argc, char **argv) {
 
     bfo_adamw_hparams hp;
     memset(&hp, 0, sizeof hp);
-    check(grad_global_norm(NULL, NULL, 1.0f, NULL, NULL) == BFO_EINVAL, "grad_global_norm refuses a null table");
+    check(grad_global_norm(NULL, NULL, 1.0f, NULL, NULL, NULL) == BFO_EINVAL, "grad_global_norm refuses a null table");
     check(adamw_sr_step(NULL, NULL, NULL, NULL, NULL, NULL, &hp, NULL, NULL, 1, 0, BFO_ROUND_SR, NULL) == BFO_EINVAL,
           "adamw_sr_step refuses a null table");
     check(master_to_bf16_sr(NULL, NULL, NULL, 0, NULL) == BFO_EINVAL, "master_to_bf16_sr refuses a null table");

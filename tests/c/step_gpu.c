@@ -125,6 +125,11 @@ int main(void) {
 
     bfo_table tb = NULL;
     BFO_OK_(bfo_table_create(tab, 3, world, rank, &tb));
+    /* the eager steps bring their own norm workspace; the graph uses the table's */
+    uint64_t wsBytes = 0;
+    BFO_OK_(bfo_norm_workspace_bytes(tb, &wsBytes));
+    void *dws = NULL;
+    HIP_OK(hipMalloc(&dws, wsBytes ? wsBytes : 8));
     const bfo_adamw_hparams hp = {1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, 1};
     const oracle_hparams ohp = {1e-3f, 0.9f, 0.95f, 1e-8f, 0.1f, 1};
     int failures = 0;
@@ -133,7 +138,7 @@ int main(void) {
         seed = (1337ull << 32) | t;
         for (uint64_t j = 0; j < S; ++j) hG[j] = bf16_from(mix64((t << 40) ^ (b + j)), 0.02f);
         HIP_OK(hipMemcpyAsync(dG, hG, S * 2, hipMemcpyHostToDevice, stream));
-        BFO_OK_(grad_global_norm(tb, dG, 1.0f, dres, stream));
+        BFO_OK_(grad_global_norm(tb, dG, 1.0f, dws, dres, stream));
         BFO_OK_(adamw_sr_step(tb, dP + b, dG, dM, dm, dv, &hp, &dres->scale, NULL, t, seed, BFO_ROUND_SR, stream));
         bfo_norm_result res;
         HIP_OK(hipMemcpyAsync(&res, dres, sizeof res, hipMemcpyDeviceToHost, stream));
@@ -188,7 +193,7 @@ int main(void) {
     hipGraph_t graph;
     hipGraphExec_t exec;
     HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
-    BFO_OK_(grad_global_norm(tb, dG, 1.0f, dres, stream));
+    BFO_OK_(grad_global_norm(tb, dG, 1.0f, NULL, dres, stream));
     BFO_OK_(adamw_sr_step_scheduled(tb, dP + b, dG, dM, dm, dv, &hp, dsteps, 3, dcursor, &dres->scale, NULL,
                                     BFO_ROUND_SR, stream));
     BFO_OK_(bfo_cursor_advance(dcursor, stream));
@@ -240,6 +245,7 @@ int main(void) {
     HIP_OK(hipFree(dm));
     HIP_OK(hipFree(dv));
     HIP_OK(hipFree(dres));
+    HIP_OK(hipFree(dws));
     free(hP); free(hG); free(oP); free(gP); free(hM); free(oM); free(om); free(ov);
     free(gM); free(gm); free(gv); free(rebuilt); free(orebuilt);
     return failures ? 1 : 0;

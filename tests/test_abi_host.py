@@ -91,7 +91,7 @@ def test_table_create_rejects_bad_tables_before_touching_the_gpu(bfo):
 def test_entry_points_reject_null_table_and_bad_scalars(bfo):
     lib = bfo.library()
     hp = bfo.AdamwHParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
-    assert lib.grad_global_norm(None, None, 1.0, None, None) == bfo.EINVAL
+    assert lib.grad_global_norm(None, None, 1.0, None, None, None) == bfo.EINVAL
     assert lib.adamw_sr_step(None, None, None, None, None, None, ctypes.byref(hp), None, None, 1, 0, 0,
                              None) == bfo.EINVAL
     assert lib.master_to_bf16_sr(None, None, None, 0, None) == bfo.EINVAL

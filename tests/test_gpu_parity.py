@@ -12,6 +12,7 @@ import torch
 
 import oracle as o
 from bf16_numerics_amd import workloads as W
+from full_state import FullStateChecker, assert_counts, snapshot
 from gpu_harness import (assert_bf16_parity, assert_f32_parity, assert_norm_parity,
                          assert_state_parity, dev_bf16, dev_f32, device_state, f32, host_copy,
                          oracle_hparams, oracle_step, step_seed, u16)
@@ -232,6 +233,62 @@ def test_norm_gpt2_124m_and_shards(bfo):
     assert abs(parts - got[0]) <= 1e-12 * got[0]
 
 
+def test_norm_workspace_size_and_two_streams(bfo):
+    # The caller's workspace: its size follows the partition (none for shards
+    # of at most 8 tiles, one binary64 per 8,192-element tile, one more per
+    # 4,096 tiles above 32,768 tiles), and two norms of one table on two
+    # streams with their own workspaces give the oracle's results, bit for bit
+    # the same as one after the other.
+    for S, want in ((1, 0), (8 * 8192, 0), (8 * 8192 + 1, 9 * 8), (32768 * 8192, 32768 * 8),
+                    (32769 * 8192, (32769 + 9) * 8)):
+        T = bfo.Table([(0, S, 0)])
+        assert bfo.norm_workspace_bytes(T) == want, S
+        T.close()
+    n = 3 * (1 << 20) + 5
+    T = bfo.Table([(0, n, 1)])
+    grads = []
+    for k in range(2):
+        g = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+        W.fill_grads(torch, W.Workload("g", [("g", (n,))], grad_std=0.01 * (k + 1)), g, 0, k + 1)
+        grads.append(g)
+    ws = [bfo.new_norm_workspace(T) for _ in range(2)]
+    serial = []
+    for k in range(2):
+        r = bfo.new_norm_result(DEV)
+        bfo.grad_global_norm(T, grads[k], r, 1.0, workspace=ws[k])
+        serial.append(r.cpu().numpy().tobytes())
+    refs = [o.grad_norm(u16(g), 1.0) for g in grads]
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(2)]
+    outs = [[bfo.new_norm_result(DEV) for _ in range(20)] for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(20):                          # interleaved launches on the two streams
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                bfo.grad_global_norm(T, grads[k], outs[k][i], 1.0, workspace=ws[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        for r in outs[k]:
+            assert r.cpu().numpy().tobytes() == serial[k]
+        assert_norm_parity(bfo.read_norm_result(outs[k][0]), refs[k])
+
+
+def test_norm_max_norm_must_be_positive(bfo):
+    n = 9 * 8192 + 1                                        # 10 tiles: the two-stage path
+    T = bfo.Table([(0, n, 0)])
+    G = torch.full((n,), 0.5, dtype=torch.bfloat16, device=DEV)
+    res = bfo.new_norm_result(DEV)
+    for bad in (0.0, -1.0, float("nan"), -float("inf")):
+        with pytest.raises(bfo.BfoError) as e:
+            bfo.grad_global_norm(T, G, res, bad)
+        assert e.value.status == bfo.EINVAL, bad
+    bfo.grad_global_norm(T, G, res, float("inf"))          # +inf: no clipping
+    sumsq, norm, scale = bfo.read_norm_result(res)
+    assert sumsq == 0.25 * n and scale == 1.0
+    with pytest.raises(bfo.BfoError) as e:                  # workspace overlapping the grads
+        bfo.grad_global_norm(T, G, res, 1.0, workspace=G.view(torch.uint8))
+    assert e.value.status == bfo.EINVAL
+
+
 # --------------------------------------------------------------------- update
 
 
@@ -279,13 +336,29 @@ def test_update_ragged_modes(bfo, master, rounding, n_tiles, tail):
     run_steps(bfo, w, T, o.table(w.entries()), st, h, 3, rounding=rounding, master=master)
 
 
-def test_update_gpt2_124m(bfo):
+def test_update_gpt2_124m_all_ten_steps(bfo):
+    # The whole 124M model, its 10 steps: the oracle carries its own copy of
+    # the state from step to step on the host (fed the GPU's clip scale, the
+    # norms being compared separately), and after every step each element of
+    # P, M, m and v is compared with the GPU's.
     w = W.gpt2_124m()
     T = bfo.Table(w.entries())
     st = device_state(w, 0, w.n, DEV)
     h = host_copy(st)
-    stats = run_steps(bfo, w, T, o.table(w.entries()), st, h, 3)
-    print("gpt2_124m element mismatches per step:", stats, flush=True)
+    chk = FullStateChecker(o.table(w.entries()), oracle_hparams(w.hparams), w.hparams.max_norm, True, DEV)
+    res = bfo.new_norm_result(DEV)
+    for t in range(1, w.steps + 1):
+        W.fill_grads(torch, w, st["G"], 0, t)
+        bfo.grad_global_norm(T, st["G"], res, w.hparams.max_norm)
+        bfo.adamw_sr_step(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, t, step_seed(t), scale=res)
+        h["G"] = u16(st["G"])
+        got_norm = bfo.read_norm_result(res)
+        assert_norm_parity(got_norm, o.grad_norm(h["G"], w.hparams.max_norm))
+        chk.oracle_step_host(h, 0, got_norm[2], t, step_seed(t), o.ROUND_SR)
+        counts = chk.compare_host_to_device(st, h, f"gpt2_124m t={t}")
+        report(f"gpt2_124m t={t} (oracle state carried from t=1)", assert_counts(counts, w.n, f"gpt2_124m t={t}"))
+    assert got_norm[2] < 1.0                           # the clip was active
+    chk.close()
 
 
 def test_update_is_deterministic(bfo):
@@ -500,7 +573,7 @@ def test_overlapping_arrays_rejected(bfo):
         assert e.value.status == bfo.EINVAL
     lib, stream = bfo.library(), ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
     g = ctypes.c_void_p(st["G"].data_ptr())
-    assert lib.grad_global_norm(T.handle, g, ctypes.c_float(1.0), g, stream) == bfo.EINVAL
+    assert lib.grad_global_norm(T.handle, g, ctypes.c_float(1.0), None, g, stream) == bfo.EINVAL
     mp = ctypes.c_void_p(st["M"].data_ptr())
     assert lib.master_to_bf16_sr(T.handle, mp, mp, ctypes.c_uint64(1), stream) == bfo.EINVAL
     torch.cuda.synchronize()
@@ -548,11 +621,25 @@ def test_stall16m_sr_tracks_master_rne_freezes(bfo):
 # --------------------------------------------------------------------- full sizes
 
 
-def full_size_step(bfo, w, rank, steps=1, master=True, rounding=o.ROUND_SR, check=None):
+def report(what, rep):
+    """Print a full-state parity report and, when BFO_PARITY_REPORT names a
+    file, append it there as one JSON line."""
+    import json
+    import os
+    line = json.dumps({"case": what, **rep})
+    print(line, flush=True)
+    path = os.environ.get("BFO_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+def full_size_step(bfo, w, rank, steps=1, master=True, rounding=o.ROUND_SR, check=None, what=None):
     """One rank of a full-size workload in the layout the benchmark times:
     full-length P and G buffers (ZeRO-1), shard-local M, m, v.  Steps `check`
-    (default: all) are compared with the oracle: the norm over the whole
-    shard, the update on sampled windows."""
+    (default: all) are compared with the oracle over every element of the
+    shard: the state before the step is kept in device memory, and the
+    oracle steps it chunk by chunk on the host threads (full_state)."""
     check = set(range(1, steps + 1)) if check is None else set(check)
     ents = w.entries()
     T = bfo.Table(ents, w.world, rank)
@@ -566,24 +653,24 @@ def full_size_step(bfo, w, rank, steps=1, master=True, rounding=o.ROUND_SR, chec
         del P
         P = P_full[b:e]
     G = torch.empty(S, dtype=torch.bfloat16, device=DEV)
-    st = {"P": P, "M": M, "m": m, "v": v, "G": G}
+    st = {"P": P, "M": M, "m": m, "v": v}
     res = bfo.new_norm_result(DEV)
-    tbl = o.table(ents)
-    wins = windows(ents, b, e, seed=rank)
+    chk = FullStateChecker(o.table(ents), oracle_hparams(w.hparams), w.hparams.max_norm, master, DEV)
+    label = what or f"{w.name} rank {rank}/{w.world} master={master} rounding={rounding}"
     for t in range(1, steps + 1):
         W.fill_grads(torch, w, G, b, t)
-        pre = [host_copy(st, lo - b, hi - b) for lo, hi in wins] if t in check else []
+        pre = snapshot(st) if t in check else None
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
         bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, t, step_seed(t), scale=res, rounding=rounding)
         got_norm = bfo.read_norm_result(res)
         if t not in check:
             continue
-        Gh = G.cpu().view(torch.int16).numpy().view(np.uint16)
-        assert_norm_parity(got_norm, o.grad_norm(Gh, w.hparams.max_norm))
-        del Gh
-        for (lo, hi), h in zip(wins, pre):
-            oracle_step(tbl, lo, h, w.hparams, got_norm[2], t, step_seed(t), rounding)
-            assert_state_parity(host_copy(st, lo - b, hi - b), h, f"{w.name} r{rank} [{lo},{hi}) t={t}")
+        counts, sumsq = chk.check_step(pre, st, G, b, got_norm[2], t, step_seed(t), rounding)
+        del pre
+        torch.cuda.empty_cache()
+        assert_norm_parity(got_norm, (sumsq, *o.norm_from_sumsq(sumsq, w.hparams.max_norm)))
+        report(f"{label} t={t}", assert_counts(counts, S, f"{label} t={t}"))
+    chk.close()
     if w.world > 1:
         outside = torch.cat([P_full[:b], P_full[e:]]).view(torch.int16)
         assert bool((outside == 0x7FA5).all()), "a write escaped the shard"
@@ -592,8 +679,10 @@ def full_size_step(bfo, w, rank, steps=1, master=True, rounding=o.ROUND_SR, chec
 
 def test_full_size_gpt2_1p5b_shard(bfo):
     w = W.gpt2_1p5b_shard()
+    # Every rank of the 1/8 shards, two steps each, every element of P, M, m
+    # and v against the oracle.
     for rank in (1, 0, 2, 3, 4, 5, 6, 7):
-        got = full_size_step(bfo, w, rank, steps=2 if rank == 1 else 1)
+        got = full_size_step(bfo, w, rank, steps=2)
         print(f"gpt2_1p5b rank {rank}: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
 
 
@@ -630,22 +719,19 @@ def test_full_size_gpt2_1p5b_shard_in_the_benchmark_placement(bfo):
     pool = [pool_mem[k * g_stride:k * g_stride + S] for k in range(2)]
     st = {"P": P, "M": M, "m": m, "v": v}
     res = bfo.new_norm_result(DEV)
-    tbl = o.table(ents)
-    wins = windows(ents, b, e, seed=11)
+    chk = FullStateChecker(o.table(ents), oracle_hparams(w.hparams), w.hparams.max_norm, True, DEV)
     for t in (1, 2):
         G = pool[t - 1]
         W.fill_grads(torch, w, G, b, t)
-        st["G"] = G
-        pre = [host_copy(st, lo - b, hi - b) for lo, hi in wins]
+        pre = snapshot(st)
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
         bfo.adamw_sr_step(T, P, G, M, m, v, w.hparams, t, step_seed(t), scale=res)
         got_norm = bfo.read_norm_result(res)
-        Gh = G.cpu().view(torch.int16).numpy().view(np.uint16)
-        assert_norm_parity(got_norm, o.grad_norm(Gh, w.hparams.max_norm))
-        del Gh
-        for (lo, hi), h in zip(wins, pre):
-            oracle_step(tbl, lo, h, w.hparams, got_norm[2], t, step_seed(t), o.ROUND_SR)
-            assert_state_parity(host_copy(st, lo - b, hi - b), h, f"spread [{lo},{hi}) t={t}")
+        counts, sumsq = chk.check_step(pre, st, G, b, got_norm[2], t, step_seed(t), o.ROUND_SR)
+        del pre
+        assert_norm_parity(got_norm, (sumsq, *o.norm_from_sumsq(sumsq, w.hparams.max_norm)))
+        report(f"gpt2_1p5b_shard rank {w.rank} spread placement t={t}", assert_counts(counts, S, f"spread t={t}"))
+    chk.close()
     outside = torch.cat([P_full[:b], P_full[e:]]).view(torch.int16)
     assert bool((outside == 0x7FA5).all()), "a write escaped the shard"
     del arrays, P_full, pool_mem, M, m, v, P, pool, st
@@ -668,14 +754,16 @@ def test_full_size_rebuild_gpt2_1p5b_shard(bfo):
     P2 = torch.zeros_like(P)
     bfo.master_to_bf16_sr(T, M, P2, step_seed(1))
     assert torch.equal(P2.view(torch.int16), P.view(torch.int16))
-    for lo, hi in windows(ents, b, e, seed=5):
-        ref = o.master_to_bf16_sr(f32(M[lo - b:hi - b]), lo, step_seed(1))
-        assert np.array_equal(u16(P2[lo - b:hi - b]), ref), (lo, hi)
+    chk = FullStateChecker(o.table(ents), oracle_hparams(w.hparams), w.hparams.max_norm, True, DEV)
+    assert chk.check_rebuild(M, P2, b, step_seed(1)) == e - b           # every element, bit for bit
+    chk.close()
 
 
+@pytest.mark.timeout(900)
 def test_full_size_llama7b(bfo):
     # 20 steps of the 6.74e9-element state (all in one shard, past 2^32
-    # elements); steps 1, 2, 10 and 20 compared with the oracle.
+    # elements); steps 1, 2, 10 and 20 compared with the oracle over every
+    # element (the pre-step state is kept beside the live one: 94 GB more).
     w = W.llama7b()
     got = full_size_step(bfo, w, 0, steps=20, check=(1, 2, 10, 20))
     print(f"llama7b: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
