@@ -38,7 +38,7 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
            "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
            "bfo_stream_mix", "bfo_plan_runs", "bfo_step_scalars_fill", "adamw_sr_step_scheduled",
-           "bfo_cursor_advance", "bfo_spread_layout", "bfo_norm_workspace_bytes")
+           "bfo_cursor_advance", "bfo_spread_layout", "bfo_norm_workspace_bytes", "grad_global_norm_noalloc")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -105,6 +105,7 @@ def _lib():
         "bfo_table_info": (i32, [vp, pu64, pu64, pu64]),
         "grad_global_norm": (i32, [vp, vp, ctypes.c_float, vp, vp, vp]),
         "bfo_norm_workspace_bytes": (i32, [vp, pu64]),
+        "grad_global_norm_noalloc": (i32, [vp, vp, ctypes.c_float, vp, vp]),
         "adamw_sr_step": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, vp, u64, u64, i32, vp]),
         "bfo_lr_at": (i32, [ctypes.POINTER(LrSchedule), u64, ctypes.POINTER(ctypes.c_float)]),
         "bfo_outlier_create": (i32, [u32, ctypes.c_float, ctypes.POINTER(vp)]),
@@ -318,6 +319,20 @@ def grad_global_norm(table, grads, out, max_norm=1.0, workspace=None):
     with torch.cuda.device(dev):
         _check("grad_global_norm", _lib().grad_global_norm(table.handle, g, max_norm, ws,
                                                            ctypes.c_void_p(out.data_ptr()), _stream(dev)))
+    return out
+
+
+def grad_global_norm_noalloc(table, grads, out, max_norm=1.0):
+    """grad_global_norm with the library's fixed device array as workspace
+    (allocates nothing; calls on one GPU must not overlap in time)."""
+    dev = table.device
+    g = _arg(grads, torch.bfloat16, table.pg_size, "grads", dev)
+    if out.dtype != torch.float64 or out.numel() != 2 or out.device != dev:
+        raise ValueError("out must be new_norm_result(device)")
+    with torch.cuda.device(dev):
+        _check("grad_global_norm_noalloc", _lib().grad_global_norm_noalloc(table.handle, g, max_norm,
+                                                                           ctypes.c_void_p(out.data_ptr()),
+                                                                           _stream(dev)))
     return out
 
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -405,6 +406,51 @@ int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, voi
     hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0,
                                     table->layout == BFO_LAYOUT_FLAT, max_norm, partials, out,
                                     static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Per-device address of the library's fixed norm array, looked up once per
+// device (with that device current) on the first allocation-free call there.
+constexpr int kMaxDevices = 64;
+std::mutex gScratchLock;
+void *gScratch[kMaxDevices] = {};
+
+int staticScratch(int device, void **out) {
+    if (device < 0 || device >= kMaxDevices) return BFO_EDEVICE;
+    std::lock_guard<std::mutex> hold(gScratchLock);
+    if (!gScratch[device]) {
+        void *p = nullptr;
+        const hipError_t he = bfo::staticScratchAddress(&p);
+        if (he != hipSuccess) return hipFail(he);
+        gScratch[device] = p;
+    }
+    *out = gScratch[device];
+    return BFO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int grad_global_norm_noalloc(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
+                             void *stream) {
+    if (!table || !out || (table->S && !grads)) return BFO_EINVAL;
+    if (table->S > bfo::kStaticNormMaxElems) return BFO_ERANGE;
+    if (!(max_norm > 0.0f)) return BFO_EINVAL;
+    if (!alignedTo(grads, 2) || !alignedTo(out, 16)) return BFO_EMISALIGNED;
+    if (anyOverlap({span(grads, 2 * pgElems(table)), span(out, sizeof(bfo_norm_result))})) return BFO_EINVAL;
+    int rc = checkDevice(table);
+    if (rc != BFO_OK) return rc;
+    void *partials = nullptr;
+    rc = staticScratch(table->device, &partials);
+    if (rc != BFO_OK) return rc;
+    hipError_t he = bfo::launchNorm(grads, table->S, table->view(), alignedTo(grads, 16) ? 1 : 0,
+                                    table->layout == BFO_LAYOUT_FLAT, max_norm, static_cast<double *>(partials),
+                                    out, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 

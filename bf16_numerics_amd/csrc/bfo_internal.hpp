@@ -46,6 +46,14 @@ inline uint64_t normWorkspaceBytes(uint64_t S) {
     return t <= kNormSmallTiles ? 0 : (t + normRuns(t)) * sizeof(double);
 }
 
+// The allocation-free norm entry point keeps its partials in a fixed device
+// array of the library (one per GPU): 2^20 binary64 values, enough for the
+// partition of any shard up to kStaticNormMaxElems elements.
+constexpr uint64_t kStaticScratchBytes = uint64_t(8) << 20;
+constexpr uint64_t kStaticNormMaxElems = uint64_t(1048320) * kNormTileVecs * 8;
+// Device address of that array on the current device (bfo_kernels.hip).
+hipError_t staticScratchAddress(void **out);
+
 // Device view of a table's shard plan.  A run is a stretch of shard-local
 // elements [local[k], local[k+1]) that sits at consecutive positions of the
 // caller's params/grads arrays (starting at addr[k]) and of the flat buffer

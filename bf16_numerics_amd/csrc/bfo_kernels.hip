@@ -791,6 +791,12 @@ __global__ __launch_bounds__(kBlock) void decayDumpKernel(ShardView sv, uint64_t
     }
 }
 
+// Partials of grad_global_norm_noalloc: a fixed array that every GPU the
+// library runs on holds until the process ends.  Host code must not pass its
+// name to a kernel (in host code it is a stand-in, not a device address):
+// staticScratchAddress gives the address on the current device.
+static __device__ __align__(256) double scratch[kStaticScratchBytes / sizeof(double)];
+
 // A launch's lane count must stay below 2^32: split long 1-D grids.
 constexpr uint64_t kMaxBlocksPerLaunch = uint64_t(1) << 22;
 
@@ -907,6 +913,8 @@ __global__ __launch_bounds__(64) void cursorAdvanceKernel(uint64_t *cursor) {
 }
 
 }  // namespace
+
+hipError_t staticScratchAddress(void **out) { return hipGetSymbolAddress(out, HIP_SYMBOL(scratch)); }
 
 hipError_t launchNorm(const uint16_t *g, uint64_t S, ShardView sv, int pgVec, bool flat, float maxNorm,
                       double *partials, bfo_norm_result *out, hipStream_t stream) {

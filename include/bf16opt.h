@@ -215,6 +215,51 @@ int bfo_norm_workspace_bytes(bfo_table table, uint64_t *bytes);
 int grad_global_norm(bfo_table table, const uint16_t *grads, float max_norm, void *workspace,
                      bfo_norm_result *out, void *stream);
 
+/* grad_global_norm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, partition and bits, with the partials kept in
+ * a fixed 8 MiB device array of the library instead of a workspace.  Every
+ * GPU the library runs on holds its own copy of that array until the process
+ * ends; its address is looked up on the first call on each device.  The call
+ * allocates nothing.  Shards of up to 8,587,837,440 elements (1,048,320
+ * norm tiles); larger ones -> BFO_ERANGE.  The array keeps the last call's
+ * partials, which nothing reads (each call writes every partial it reads),
+ * but all calls on one GPU share it: calls whose GPU work overlaps in time
+ * on one GPU (different streams without ordering, or several threads) race
+ * and give wrong norms.  Other arguments and errors as grad_global_norm. */
+int grad_global_norm_noalloc(bfo_table table, const uint16_t *grads, float max_norm, bfo_norm_result *out,
+                             void *stream);
+
+/* One AdamW step over the shard ("04 · 多 GPU 与混合精度" §2.2, with the
+ * lerp computed as two fused multiply-adds; "第 13 讲" §1.7 for bias
+ * correction and decoupled decay).  Per element i (global) / j (local):
+ *   g   = scale * f32(grads[j])
+ *   m1  = fma(b1, m[j], fma(-b1, g, g));  v1 = fma(b2, v[j], fma(-b2, g*g, g*g))
+ *   mh  = m1 / bc1;  vh = v1 / bc2;  u = mh / (sqrt(vh) + eps)
+ *   old = master ? master[j] : f32(params[j])
+ *   p   = old - lr * (u + w_i * old),  w_i = weight_decay if i's tensor has
+ *         BFO_FLAG_DECAY else 0
+ *   m[j] = m1; v[j] = v1; master[j] = p (when master != NULL);
+ *   params[j] = SR(p, r16(i, seed)) or RNE(p)
+ * each a single binary32 operation in that order.  bc1/bc2 =
+ * (float)(1 - pow(beta, t)) in binary64, or 1 when bias correction is off.
+ * SR rounds to the next bf16 away from zero when the 16 discarded bits of p
+ * exceed r16, else truncates; r16 is a 16-bit draw of Philox4x32-10 (Salmon
+ * et al., SC'11) with counter (lo32(i>>3), hi32(i>>3), 0, 0) and key
+ * (lo32(seed), hi32(seed)); element i takes output word (i>>1)&3, low half
+ * for even i.  RNE rounds to nearest, ties to even.  NaN stays NaN.
+ * i is element j's global index (its run's global + offset), so every
+ * layout and shard count draws the same r16 for the same parameter.
+ * master == NULL selects the no-master path (old weights read from params).
+ * scale: device float (e.g. &out->scale of grad_global_norm), or NULL for 1.
+ * skip: device int32 (e.g. written by bfo_outlier_update), or NULL; when it
+ * holds a nonzero value at run time the step changes nothing (every
+ * workgroup exits after reading it).
+ * t: 1-based step number (0 -> BFO_EINVAL).  rounding: BFO_ROUND_SR/RNE. */
+int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                  float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
+                  uint64_t seed, int rounding, void *stream);
+
 /* One AdamW step over the shard ("04 · 多 GPU 与混合精度" §2.2, with the
  * lerp computed as two fused multiply-adds; "第 13 讲" §1.7 for bias
  * correction and decoupled decay).  Per element i (global) / j (local):
