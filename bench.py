@@ -121,22 +121,29 @@ def cpu_baseline(torch, w, st, begin, target_s, rounding_sr=True):
             "single_thread_value": one}
 
 
-def checkpoint_rate(torch, bfo, T, P, M, m, v, seed, directory):
+def checkpoint_rate(torch, bfo, T, P, M, m, v, seed, rounding, directory):
     """Save this rank's optimizer state, mark it done, find it as the latest,
-    load it into fresh buffers and check every byte; time save and load."""
+    load it into fresh buffers (with a master, the params are rebuilt from it
+    during the load) and check every byte; time save and load."""
     import shutil
 
     step_no = 1
     os.makedirs(directory, exist_ok=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    bfo.checkpoint_save(directory, T, m, v, step_no, seed, master=M, params=None if M is not None else P)
+    bfo.checkpoint_save(directory, T, m, v, step_no, seed, master=M, params=None if M is not None else P,
+                        rounding=rounding)
     bfo.checkpoint_done(directory, step_no)
     t_save = time.perf_counter() - t0
     assert bfo.checkpoint_latest(directory) == step_no
     m2, v2 = torch.empty_like(m), torch.empty_like(v)
     M2 = torch.empty_like(M) if M is not None else None
-    P2 = torch.empty_like(P) if M is None else None
+    # the shard's positions of P2 start as a NaN pattern; the load must fill them
+    P2 = P.clone()
+    if T.layout == bfo.LAYOUT_PER_TENSOR:
+        P2.view(torch.int16)[torch.from_numpy(T.global_index().astype("int64")).to(P.device)] = 0x7FA5
+    else:
+        P2.view(torch.int16).fill_(0x7FA5)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     got_seed = bfo.checkpoint_load(directory, step_no, T, m2, v2, master=M2, params=P2)
@@ -144,8 +151,7 @@ def checkpoint_rate(torch, bfo, T, P, M, m, v, seed, directory):
     t_load = time.perf_counter() - t0
     same = got_seed == seed and all(torch.equal(a.view(torch.int32), b.view(torch.int32))
                                    for a, b in ((m, m2), (v, v2)) + (((M, M2),) if M is not None else ()))
-    if M is None:
-        same = same and torch.equal(P.view(torch.int16), P2.view(torch.int16))
+    same = same and torch.equal(P.view(torch.int16), P2.view(torch.int16))
     nbytes = sum(os.path.getsize(os.path.join(directory, f)) for f in os.listdir(directory))
     shutil.rmtree(directory, ignore_errors=True)
     del m2, v2, M2, P2
@@ -275,6 +281,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="record the step once per grads buffer as a HIP graph (norm, outlier update, scheduled "
                          "update, cursor advance) and time graph replays")
+    ap.add_argument("--one-call", action="store_true",
+                    help="each step is one adamw_sr_step_with_norm call (norm, clip and update; a single kernel "
+                         "launch for shards of at most 65,536 elements) instead of grad_global_norm + adamw_sr_step")
     ap.add_argument("--placement", choices=("spread", "packed"), default="spread",
                     help="spread: params, grads, master, m and v carved from one arena covering most of device "
                          "memory, each starting on its own 16 GiB boundary (bfo_spread_layout); packed: one "
@@ -291,6 +300,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the step is measured on one "
               "GPU's ZeRO-1 shard; no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
+
+    if args.one_call and (args.graph or args.step_control):
+        ap.error("--one-call takes the clip scale from its own norm: no --graph or --step-control")
 
     import torch
     from bf16_numerics_amd import binding as bfo
@@ -341,11 +353,15 @@ def main():
         W.fill_grads(torch, w, G, g_begin, k + 1)
     torch.cuda.empty_cache()
     res = bfo.new_norm_result(dev)
+    norm_ws = bfo.new_norm_workspace(T)
     hp = bfo.AdamwHParams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps,
                           w.hparams.weight_decay, 1)
     stream = torch.cuda.current_stream(dev)
     rounding = bfo.ROUND_RNE if args.rounding == "rne" else bfo.ROUND_SR
     upd_bytes = UPDATE_BYTES_NO_MASTER if args.no_master else UPDATE_BYTES
+    step_bytes = upd_bytes + NORM_BYTES
+    if args.one_call:
+        upd_bytes = step_bytes           # the timed call reads the grads for the norm too
     variant = ("no-master" if args.no_master else "master") + "," + args.rounding.upper()
     last_t = args.warmup + 2 * args.steps + 1   # warm-up, timed, lead, event-bracketed steps
     outlier, hps = None, None
@@ -380,7 +396,7 @@ def main():
                               rounding=rounding, skip=skip)
 
     def record_step(G):
-        bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
+        bfo.grad_global_norm(T, G, res, w.hparams.max_norm, workspace=norm_ws)
         return outlier.update(bfo.norm_ptr(res)).skip if outlier is not None else None
 
     graphs = []
@@ -401,6 +417,14 @@ def main():
             return
         if ev is not None:
             ev[2].record(stream)
+        if args.one_call:
+            if ev is not None:
+                ev[0].record(stream)
+            bfo.adamw_sr_step_with_norm(T, P, G, M, m, v, hp, t, (1337 << 32) | t, res, w.hparams.max_norm,
+                                        rounding=rounding, workspace=norm_ws)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         skip = record_step(G)
         if ev is not None:
             ev[0].record(stream)
@@ -456,10 +480,11 @@ def main():
     norm_ms = [s0.elapsed_time(a) for a, _, s0 in evs]
     step_ev_ms = sorted(s0.elapsed_time(z) for _, z, s0 in evs)
     gparams = S / (ms_step * 1e-3) / 1e9
-    step_gbs = (upd_bytes + NORM_BYTES) * S / (ms_step * 1e-3) / 1e9
+    step_gbs = step_bytes * S / (ms_step * 1e-3) / 1e9
     achieved = upd_bytes * S / (upd_avg * 1e-3) / 1e9
     default_variant = (args.layout == "flat" and not args.pad and not args.no_master and args.rounding == "sr"
-                       and args.rank is None and not args.graph and args.placement == "spread")
+                       and args.rank is None and not args.graph and args.placement == "spread"
+                       and not args.one_call)
     traffic = measured_traffic(w.name) if default_variant else None
     last_seed = (1337 << 32) | last_t      # seed of the last update (the check pass repeats the same t)
     sumsq, norm, scale = bfo.read_norm_result(res)
@@ -480,12 +505,16 @@ def main():
         "config": {"workload": w.name + (f"+pad{args.pad}" if args.pad else ""), "n_total": w.n,
                    "layout": args.layout, "shard": [b, e], "shard_elems": S,
                    "world": w.world, "rank": w.rank, "tensors": len(w.tensors),
-                   "grad_pool": len(pool), "bytes_per_param_step": upd_bytes + NORM_BYTES,
-                   "update": variant, "launch": "graph" if args.graph else "stream",
+                   "grad_pool": len(pool), "bytes_per_param_step": step_bytes,
+                   "update": variant,
+                   "launch": "graph" if args.graph else ("one-call" if args.one_call else "stream"),
                    "placement": args.placement, "arena_bytes": arrays["arena_bytes"]},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": f"adamwTileKernel<{variant}{',scheduled' if args.graph else ''}>",
+        "roofline": {"bound": "hbm",
+                     "kernel": (f"adamw_sr_step_with_norm<{variant}> (norm + update"
+                                f"{', one launch' if S <= 65536 else ''})") if args.one_call else
+                               f"adamwTileKernel<{variant}{',scheduled' if args.graph else ''}>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "target_frac": TARGET_FRAC,
@@ -504,7 +533,7 @@ def main():
                                "z_threshold": 6.0, "last_z": float(outlier.z.item()),
                                "skipped_in_check_pass": int(skips.item())}
     if args.checkpoint_dir:
-        out["checkpoint"] = checkpoint_rate(torch, bfo, T, P, M, m, v, last_seed, args.checkpoint_dir)
+        out["checkpoint"] = checkpoint_rate(torch, bfo, T, P, M, m, v, last_seed, rounding, args.checkpoint_dir)
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

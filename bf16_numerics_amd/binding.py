@@ -38,7 +38,8 @@ EXPORTS = ("shard_range", "bfo_table_create", "bfo_table_create_layout", "bfo_ta
            "bfo_outlier_create", "bfo_outlier_destroy", "bfo_outlier_reset", "bfo_outlier_update",
            "bfo_checkpoint_save", "bfo_checkpoint_done", "bfo_checkpoint_latest", "bfo_checkpoint_load",
            "bfo_stream_mix", "bfo_plan_runs", "bfo_step_scalars_fill", "adamw_sr_step_scheduled",
-           "bfo_cursor_advance", "bfo_spread_layout", "bfo_norm_workspace_bytes", "grad_global_norm_noalloc")
+           "bfo_cursor_advance", "bfo_spread_layout", "bfo_norm_workspace_bytes", "grad_global_norm_noalloc", "master_to_bf16",
+           "bfo_checksum64", "adamw_sr_step_with_norm")
 
 LR_CONSTANT, LR_LINEAR, LR_COSINE, LR_WSD = 0, 1, 2, 3
 
@@ -107,12 +108,16 @@ def _lib():
         "bfo_norm_workspace_bytes": (i32, [vp, pu64]),
         "grad_global_norm_noalloc": (i32, [vp, vp, ctypes.c_float, vp, vp]),
         "adamw_sr_step": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), vp, vp, u64, u64, i32, vp]),
+        "adamw_sr_step_with_norm": (i32, [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamwHParams), ctypes.c_float, vp,
+                                          vp, vp, u64, u64, i32, vp]),
         "bfo_lr_at": (i32, [ctypes.POINTER(LrSchedule), u64, ctypes.POINTER(ctypes.c_float)]),
         "bfo_outlier_create": (i32, [u32, ctypes.c_float, ctypes.POINTER(vp)]),
         "bfo_outlier_destroy": (i32, [vp]),
         "bfo_outlier_reset": (i32, [vp, vp]),
         "bfo_outlier_update": (i32, [vp, vp, vp, vp, vp]),
-        "bfo_checkpoint_save": (i32, [ctypes.c_char_p, vp, vp, vp, vp, vp, u64, u64, vp]),
+        "bfo_checkpoint_save": (i32, [ctypes.c_char_p, vp, vp, vp, vp, vp, u64, u64, i32, vp]),
+        "bfo_checksum64": (u64, [vp, u64]),
+        "master_to_bf16": (i32, [vp, vp, vp, u64, i32, vp]),
         "bfo_checkpoint_done": (i32, [ctypes.c_char_p, u64]),
         "bfo_checkpoint_latest": (i32, [ctypes.c_char_p, pu64]),
         "bfo_checkpoint_load": (i32, [ctypes.c_char_p, u64, vp, vp, vp, vp, vp, pu64, vp]),
@@ -368,6 +373,27 @@ def adamw_sr_step(table, params, grads, master, m, v, hp, t, seed, scale=None,
                                                      t, seed, rounding, _stream(dev)))
 
 
+def adamw_sr_step_with_norm(table, params, grads, master, m, v, hp, t, seed, out, max_norm=1.0,
+                            rounding=ROUND_SR, skip=None, workspace=None):
+    """grad_global_norm into `out` (a norm-result buffer) and the update with
+    its scale, in one call (one launch for shards of at most 65,536 elements)."""
+    dev = table.device
+    S = table.size
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
+    g = _arg(grads, torch.bfloat16, table.pg_size, "grads", dev)
+    M = _arg(master, torch.float32, S, "master", dev)
+    mm = _arg(m, torch.float32, S, "m", dev)
+    vv = _arg(v, torch.float32, S, "v", dev)
+    if out.dtype != torch.float64 or out.numel() != 2 or out.device != dev:
+        raise ValueError("out must be new_norm_result(device)")
+    sk = _arg(skip, torch.int32, 1, "skip", dev) if skip is not None else None
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    with torch.cuda.device(dev):
+        _check("adamw_sr_step_with_norm", _lib().adamw_sr_step_with_norm(
+            table.handle, p, g, M, mm, vv, ctypes.byref(_hparams(hp)), max_norm, ws,
+            ctypes.c_void_p(out.data_ptr()), sk, t, seed, rounding, _stream(dev)))
+
+
 def _hparams(hp):
     if isinstance(hp, AdamwHParams):
         return hp
@@ -497,6 +523,20 @@ def master_to_bf16_sr(table, master, params, seed):
         _check("master_to_bf16_sr", _lib().master_to_bf16_sr(table.handle, M, p, seed, _stream(dev)))
 
 
+def master_to_bf16(table, master, params, seed, rounding=ROUND_SR):
+    dev = table.device
+    M = _arg(master, torch.float32, table.size, "master", dev)
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
+    with torch.cuda.device(dev):
+        _check("master_to_bf16", _lib().master_to_bf16(table.handle, M, p, seed, rounding, _stream(dev)))
+
+
+def checksum64(data):
+    """bfo_checksum64 of a bytes-like object (host only)."""
+    buf = (ctypes.c_char * len(data)).from_buffer_copy(bytes(data))
+    return _lib().bfo_checksum64(buf, len(data))
+
+
 def rng_dump(first, count, seed, device=None):
     dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index or 0)
     out = torch.empty(count, dtype=torch.int16, device=dev)
@@ -529,16 +569,17 @@ def stream_mix(params, grads, master, m, v, key=0):
         _check("bfo_stream_mix", _lib().bfo_stream_mix(*args, count, key & 0xFFFFFFFF, _stream(dev)))
 
 
-def checkpoint_save(directory, table, m, v, step, seed, master=None, params=None):
-    """Write this rank's state of `step` (master, or params when master is None)."""
+def checkpoint_save(directory, table, m, v, step, seed, master=None, params=None, rounding=ROUND_SR):
+    """Write this rank's state of `step`: master and/or params (at least one),
+    m, v, and the seed and rounding mode of the last update."""
     dev = table.device
     M = _arg(master, torch.float32, table.size, "master", dev)
-    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev) if master is None else None
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
     mm = _arg(m, torch.float32, table.size, "m", dev)
     vv = _arg(v, torch.float32, table.size, "v", dev)
     with torch.cuda.device(dev):
         _check("bfo_checkpoint_save", _lib().bfo_checkpoint_save(os.fsencode(directory), table.handle, p, M, mm, vv,
-                                                               step, seed, _stream(dev)))
+                                                               step, seed, rounding, _stream(dev)))
 
 
 def checkpoint_done(directory, step):
@@ -556,10 +597,11 @@ def checkpoint_latest(directory):
 
 
 def checkpoint_load(directory, step, table, m, v, master=None, params=None):
-    """Read this rank's state of `step`; returns the saved seed."""
+    """Read this rank's state of `step` (params stored or rebuilt from the
+    stored master when given); returns the saved seed."""
     dev = table.device
     M = _arg(master, torch.float32, table.size, "master", dev)
-    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev) if master is None else None
+    p = _arg(params, torch.bfloat16, table.pg_size, "params", dev)
     mm = _arg(m, torch.float32, table.size, "m", dev)
     vv = _arg(v, torch.float32, table.size, "v", dev)
     seed = ctypes.c_uint64(0)

@@ -75,6 +75,14 @@ struct bfo_table_s {
 // flat tables, the whole buffer for per-tensor ones.
 static uint64_t pgElems(const bfo_table_s *t) { return t->layout == BFO_LAYOUT_FLAT ? t->S : t->n; }
 
+int bfo::rebuildParams(bfo_table_s *t, const float *master, uint16_t *params, uint64_t seed, int rounding,
+                       hipStream_t stream) {
+    if (t->S == 0) return BFO_OK;
+    const int pgVec = (reinterpret_cast<uintptr_t>(params) & 15) == 0 ? 1 : 0;
+    const hipError_t he = launchMasterToBf16(master, params, t->S, t->view(), pgVec, seed, rounding, stream);
+    return he == hipSuccess ? BFO_OK : recordHipFailure(he);
+}
+
 bfo::TableFacts bfo::tableFacts(const bfo_table_s *t) {
     return {t->n, t->S, t->world, t->rank, t->layout, t->fingerprint, t->runs.data(), uint32_t(t->runs.size())};
 }
@@ -358,22 +366,33 @@ bfo::StepScalars stepScalars(const bfo_adamw_hparams &hp, float lr, float bc1, f
 }
 
 // Validation and launch shared by adamw_sr_step and adamw_sr_step_scheduled.
-int launchStep(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m, float *v,
-               const bfo::StepScalars &s, const float *scale, const int32_t *skip, uint64_t seed, int rounding,
-               const bfo::StepSchedule *sched, void *stream) {
+// Argument checks of an update (and, for the one-call step, of its norm:
+// `out` and `workspace`, which must not overlap the arrays either).
+int checkStep(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m, float *v,
+              const float *scale, const int32_t *skip, int rounding, const bfo_norm_result *out = nullptr,
+              const void *workspace = nullptr) {
     if (!table) return BFO_EINVAL;
     if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
     const uint64_t S = table->S;
     if (S && (!params || !grads || !m || !v)) return BFO_EINVAL;
     if (!alignedTo(params, 2) || !alignedTo(grads, 2) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
-        !alignedTo(v, 16) || !alignedTo(scale, 4) || !alignedTo(skip, 4))
+        !alignedTo(v, 16) || !alignedTo(scale, 4) || !alignedTo(skip, 4) || !alignedTo(out, 16) ||
+        !alignedTo(workspace, 8))
         return BFO_EMISALIGNED;
     const uint64_t pg = 2 * pgElems(table);
     if (anyOverlap({span(params, pg), span(grads, pg), span(master, 4 * S), span(m, 4 * S), span(v, 4 * S),
-                    span(scale, 4), span(skip, 4)}))
+                    span(scale, 4), span(skip, 4), span(out, sizeof(bfo_norm_result)),
+                    span(workspace, bfo::normWorkspaceBytes(S))}))
         return BFO_EINVAL;
-    int rc = checkDevice(table);
+    return checkDevice(table);
+}
+
+int launchStep(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m, float *v,
+               const bfo::StepScalars &s, const float *scale, const int32_t *skip, uint64_t seed, int rounding,
+               const bfo::StepSchedule *sched, void *stream) {
+    int rc = checkStep(table, params, grads, master, m, v, scale, skip, rounding);
     if (rc != BFO_OK) return rc;
+    const uint64_t S = table->S;
     if (S == 0) return BFO_OK;
     const int pgVec = alignedTo(params, 16) && alignedTo(grads, 16) ? 1 : 0;
     hipError_t he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, scale, skip, seed,
@@ -463,6 +482,35 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
     return launchStep(table, params, grads, master, m, v, s, scale, skip, seed, rounding, nullptr, stream);
 }
 
+int adamw_sr_step_with_norm(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                            float *v, const bfo_adamw_hparams *hp, float max_norm, void *workspace,
+                            bfo_norm_result *out, const int32_t *skip, uint64_t t, uint64_t seed, int rounding,
+                            void *stream) {
+    if (!hp || t == 0 || !out || !(max_norm > 0.0f)) return BFO_EINVAL;
+    int rc = checkStep(table, params, grads, master, m, v, nullptr, skip, rounding, out, workspace);
+    if (rc != BFO_OK) return rc;
+    const bfo::StepScalars s = stepScalars(*hp, hp->lr, biasCorrection(hp->beta1, t, hp->bias_correction),
+                                           biasCorrection(hp->beta2, t, hp->bias_correction));
+    const uint64_t S = table->S;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int gVec = alignedTo(grads, 16) ? 1 : 0;
+    const int pgVec = gVec && alignedTo(params, 16) ? 1 : 0;
+    const bool flat = table->layout == BFO_LAYOUT_FLAT;
+    const uint64_t ntiles = bfo::normTiles(S);
+    hipError_t he;
+    if (ntiles > 0 && ntiles <= bfo::kNormSmallTiles) {
+        he = bfo::launchSmallStep(params, grads, master, m, v, S, table->view(), gVec, pgVec, flat, max_norm, out, s,
+                                  skip, seed, rounding, st);
+    } else {
+        double *partials = workspace ? static_cast<double *>(workspace) : table->normPartials;
+        he = bfo::launchNorm(grads, S, table->view(), gVec, flat, max_norm, partials, out, st);
+        if (he == hipSuccess && S)
+            he = bfo::launchAdamw(params, grads, master, m, v, S, table->view(), pgVec, s, &out->scale, skip, seed,
+                                  rounding, nullptr, st);
+    }
+    return he == hipSuccess ? BFO_OK : hipFail(he);
+}
+
 int bfo_step_scalars_fill(const bfo_adamw_hparams *hp, uint64_t t, float lr, uint64_t seed,
                           bfo_step_scalars *out) {
     if (!hp || !out || t == 0) return BFO_EINVAL;
@@ -500,19 +548,22 @@ int bfo_cursor_advance(uint64_t *cursor, void *stream) {
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 
-int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
-                      void *stream) {
+int master_to_bf16(bfo_table table, const float *master, uint16_t *params, uint64_t seed, int rounding,
+                   void *stream) {
     if (!table) return BFO_EINVAL;
+    if (rounding != BFO_ROUND_SR && rounding != BFO_ROUND_RNE) return BFO_EINVAL;
     const uint64_t S = table->S;
     if (S && (!master || !params)) return BFO_EINVAL;
     if (!alignedTo(master, 16) || !alignedTo(params, 2)) return BFO_EMISALIGNED;
     if (anyOverlap({span(master, 4 * S), span(params, 2 * pgElems(table))})) return BFO_EINVAL;
     int rc = checkDevice(table);
     if (rc != BFO_OK) return rc;
-    if (S == 0) return BFO_OK;
-    hipError_t he = bfo::launchMasterToBf16(master, params, S, table->view(), alignedTo(params, 16) ? 1 : 0,
-                                            seed, static_cast<hipStream_t>(stream));
-    return he == hipSuccess ? BFO_OK : hipFail(he);
+    return bfo::rebuildParams(table, master, params, seed, rounding, static_cast<hipStream_t>(stream));
+}
+
+int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
+                      void *stream) {
+    return master_to_bf16(table, master, params, seed, BFO_ROUND_SR, stream);
 }
 
 int bfo_rng_dump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out, void *stream) {

@@ -102,6 +102,10 @@ struct TableFacts {
     uint32_t nruns;
 };
 TableFacts tableFacts(const bfo_table_s *table);
+// master_to_bf16 without the host-side argument checks (the checkpoint
+// loader, which has checked its own arguments).
+int rebuildParams(bfo_table_s *table, const float *master, uint16_t *params, uint64_t seed, int rounding,
+                  hipStream_t stream);
 
 // Launchers (bfo_kernels.hip).  Shapes are checked by the caller: M, m, v
 // hold S shard-local elements, 16-byte aligned; P and G are addressed
@@ -115,8 +119,13 @@ hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float
                        ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
                        uint64_t seed, int rounding, const StepSchedule *sched, hipStream_t stream);
 hipError_t launchCursorAdvance(uint64_t *cursor, hipStream_t stream);
+// Norm, clip scale and update in one launch, for 0 < normTiles(S) <= kNormSmallTiles.
+// gVec: G 16-byte aligned (the norm's fast path); pgVec as for launchAdamw.
+hipError_t launchSmallStep(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S, ShardView sv,
+                           int gVec, int pgVec, bool flat, float maxNorm, bfo_norm_result *out, StepScalars s,
+                           const int32_t *skip, uint64_t seed, int rounding, hipStream_t stream);
 hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
-                              uint64_t seed, hipStream_t stream);
+                              uint64_t seed, int rounding, hipStream_t stream);
 hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t *out,
                          hipStream_t stream);
 hipError_t launchDecayDump(ShardView sv, uint64_t S, uint8_t *out, hipStream_t stream);

@@ -263,18 +263,16 @@ __device__ void adamwElementwise(uint16_t *P, const uint16_t *G, float *M, float
 // recorded launch serves every step; the cursor is read before the data
 // loads are issued and the scalars after, so their round trips overlap.
 // ---------------------------------------------------------------------------
+// The update of one tile by one workgroup (the body of adamwTileKernel and
+// of the one-launch small step).  cur: the schedule cursor, read by the
+// caller (kScheduled only).
 template <bool kMaster, int kRound, bool kScheduled>
-__global__ __launch_bounds__(kBlock) void adamwTileKernel(
-    uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
-    float *__restrict__ Mom, float *__restrict__ Var, uint64_t S, ShardView sv, int pgVec, StepScalars s,
-    const float *__restrict__ scalePtr, const int32_t *__restrict__ skipPtr, uint32_t key0, uint32_t key1,
-    uint64_t tileBase, const bfo_step_scalars *__restrict__ steps, uint64_t nsteps,
-    const uint64_t *__restrict__ cursor) {
-    if (skipPtr && *skipPtr) return;  // step control decided to skip this update
-    uint64_t cur = 0;
-    if constexpr (kScheduled) cur = *cursor;
-    const float scale = scalePtr ? *scalePtr : 1.0f;
-    const uint64_t tile = tileBase + blockIdx.x;
+__device__ __forceinline__ void adamwTile(uint16_t *__restrict__ P, const uint16_t *__restrict__ G,
+                                          float *__restrict__ M, float *__restrict__ Mom, float *__restrict__ Var,
+                                          uint64_t S, const ShardView &sv, int pgVec, StepScalars s, float scale,
+                                          uint32_t key0, uint32_t key1, uint64_t tile,
+                                          const bfo_step_scalars *__restrict__ steps, uint64_t nsteps,
+                                          uint64_t cur) {
     const uint32_t tileWord = sv.tile[tile];
 
     uint4 gv[kVecPerLane], pv[kVecPerLane];
@@ -379,6 +377,21 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
     }
 }
 
+template <bool kMaster, int kRound, bool kScheduled>
+__global__ __launch_bounds__(kBlock) void adamwTileKernel(
+    uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
+    float *__restrict__ Mom, float *__restrict__ Var, uint64_t S, ShardView sv, int pgVec, StepScalars s,
+    const float *__restrict__ scalePtr, const int32_t *__restrict__ skipPtr, uint32_t key0, uint32_t key1,
+    uint64_t tileBase, const bfo_step_scalars *__restrict__ steps, uint64_t nsteps,
+    const uint64_t *__restrict__ cursor) {
+    if (skipPtr && *skipPtr) return;  // step control decided to skip this update
+    uint64_t cur = 0;
+    if constexpr (kScheduled) cur = *cursor;
+    const float scale = scalePtr ? *scalePtr : 1.0f;
+    adamwTile<kMaster, kRound, kScheduled>(P, G, M, Mom, Var, S, sv, pgVec, s, scale, key0, key1,
+                                           tileBase + blockIdx.x, steps, nsteps, cur);
+}
+
 // ---------------------------------------------------------------------------
 // Measurement kernel: the update's memory traffic without its arithmetic.
 // Same tile, lane and vector plan as the 16-byte path of adamwTileKernel
@@ -450,11 +463,12 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Rebuild bf16 weights from the master: P = SR(M, draw), same vector plan.
-// The master is only read and the params only written here: nontemporal
-// loads (4-6% faster than plain ones on this 4 B read + 2 B write pattern)
-// and nontemporal stores (a further 4-5%).
+// Rebuild bf16 weights from the master: P = SR(M, draw) (or RNE(M)), same
+// vector plan.  The master is only read and the params only written here:
+// nontemporal loads (4-6% faster than plain ones on this 4 B read + 2 B
+// write pattern) and nontemporal stores (a further 4-5%).
 // ---------------------------------------------------------------------------
+template <int kRound>
 __global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
                                                              uint16_t *__restrict__ P, uint64_t S,
                                                              ShardView sv, int pgVec, uint32_t key0,
@@ -491,20 +505,24 @@ __global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__rest
                 if (j >= S) break;
                 uint64_t addr, rng;
                 placeElement(sv, run, j, addr, rng);
-                if ((rng >> 3) != cachedGroup) {
-                    cachedGroup = rng >> 3;
-                    cached = philox10(cachedGroup, key0, key1);
+                uint32_t draw = 0;
+                if constexpr (kRound == BFO_ROUND_SR) {
+                    if ((rng >> 3) != cachedGroup) {
+                        cachedGroup = rng >> 3;
+                        cached = philox10(cachedGroup, key0, key1);
+                    }
+                    draw = drawOf(cached, int(rng & 7));
                 }
-                P[addr] = uint16_t(roundSR(M[j], drawOf(cached, int(rng & 7))));
+                P[addr] = uint16_t(writeBack<kRound>(M[j], draw));
             }
             continue;
         }
-        uint32_t d[8];
-        draws8(pl[k].rng0, key0, key1, d);
-        const uint32_t h0 = roundSR(a[k].x, d[0]), h1 = roundSR(a[k].y, d[1]);
-        const uint32_t h2 = roundSR(a[k].z, d[2]), h3 = roundSR(a[k].w, d[3]);
-        const uint32_t h4 = roundSR(b[k].x, d[4]), h5 = roundSR(b[k].y, d[5]);
-        const uint32_t h6 = roundSR(b[k].z, d[6]), h7 = roundSR(b[k].w, d[7]);
+        uint32_t d[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if constexpr (kRound == BFO_ROUND_SR) draws8(pl[k].rng0, key0, key1, d);
+        const uint32_t h0 = writeBack<kRound>(a[k].x, d[0]), h1 = writeBack<kRound>(a[k].y, d[1]);
+        const uint32_t h2 = writeBack<kRound>(a[k].z, d[2]), h3 = writeBack<kRound>(a[k].w, d[3]);
+        const uint32_t h4 = writeBack<kRound>(b[k].x, d[4]), h5 = writeBack<kRound>(b[k].y, d[5]);
+        const uint32_t h6 = writeBack<kRound>(b[k].z, d[6]), h7 = writeBack<kRound>(b[k].w, d[7]);
         if (mode[k] == kRegular) {
             storeOnce16(P, pl[k].addr0 >> 3,
                         make_uint4(h0 | (h1 << 16), h2 | (h3 << 16), h4 | (h5 << 16), h6 | (h7 << 16)));
@@ -718,6 +736,49 @@ __global__ __launch_bounds__(kNormFinishBlock) void normSmallKernel(const uint16
         out->norm = norm;
         out->scale = scale;
     }
+}
+
+// A whole small step in one launch (shards of at most kNormSmallTiles norm
+// tiles, i.e. at most 16 update tiles).  Every workgroup forms the shard's
+// sum of squares itself -- tile by tile with stage 1's lane map and tileSum,
+// then partial t in lane t of a wave (+0 elsewhere) through the same
+// butterfly as normSmallKernel's final sum, whose other waves only add +0
+// -- so its sum, norm and scale are those of the two-launch path bit for
+// bit (the grads, at most 128 KiB, come from the cache after the first
+// workgroup).  Workgroup 0 writes `out`; each workgroup then updates its own
+// tile with that scale, unless the skip flag is set.
+template <bool kMaster, int kRound>
+__global__ __launch_bounds__(kBlock) void adamwSmallStepKernel(
+    uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M, float *__restrict__ Mom,
+    float *__restrict__ Var, uint64_t S, ShardView sv, int gVec, int pgVec, int flat, uint32_t ntiles,
+    float maxNorm, bfo_norm_result *__restrict__ out, StepScalars s, const int32_t *__restrict__ skipPtr,
+    uint32_t key0, uint32_t key1) {
+    __shared__ double waveSums[kBlock / 64];
+    __shared__ double partial[kNormSmallTiles];
+    for (uint32_t tile = 0; tile < ntiles; ++tile) {
+        const double acc = (flat && gVec) ? normTileDirect(G, S, tile, threadIdx.x)
+                                          : normTilePlanned(G, S, sv, gVec, tile, threadIdx.x);
+        const double total = tileSum(acc, waveSums, 0);
+        if (threadIdx.x == 0) partial[tile] = total;
+        __syncthreads();  // partial written; waveSums free for the next tile
+    }
+    const uint32_t lane = threadIdx.x & 63;
+    double x = 0.0;
+    if (lane < ntiles) x += partial[lane];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    // every lane now holds the same sum: each butterfly stage adds the same
+    // two values on both lanes of a pair, and addition is commutative
+    const float norm = float(sqrt(x));
+    const float scale = norm > maxNorm ? maxNorm / norm : 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        out->sumsq = x;
+        out->norm = norm;
+        out->scale = scale;
+    }
+    if (skipPtr && *skipPtr) return;
+    adamwTile<kMaster, kRound, false>(P, G, M, Mom, Var, S, sv, pgVec, s, scale, key0, key1, blockIdx.x, nullptr,
+                                      0, 0);
 }
 
 __global__ __launch_bounds__(kBlock) void normReduceKernel(const double *__restrict__ in, uint64_t count,
@@ -956,6 +1017,28 @@ hipError_t launchAdamw(uint16_t *P, const uint16_t *G, float *M, float *m, float
                                stream);
 }
 
+hipError_t launchSmallStep(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S, ShardView sv,
+                           int gVec, int pgVec, bool flat, float maxNorm, bfo_norm_result *out, StepScalars s,
+                           const int32_t *skip, uint64_t seed, int rounding, hipStream_t stream) {
+    const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
+    const uint32_t ntiles = uint32_t(normTiles(S));
+    const dim3 grid(uint32_t((S + kTileElems - 1) / kTileElems)), block(kBlock);
+    const int fl = flat ? 1 : 0;
+    if (M && rounding == BFO_ROUND_SR)
+        hipLaunchKernelGGL((adamwSmallStepKernel<true, BFO_ROUND_SR>), grid, block, 0, stream, P, G, M, m, v, S, sv,
+                           gVec, pgVec, fl, ntiles, maxNorm, out, s, skip, k0, k1);
+    else if (M)
+        hipLaunchKernelGGL((adamwSmallStepKernel<true, BFO_ROUND_RNE>), grid, block, 0, stream, P, G, M, m, v, S, sv,
+                           gVec, pgVec, fl, ntiles, maxNorm, out, s, skip, k0, k1);
+    else if (rounding == BFO_ROUND_SR)
+        hipLaunchKernelGGL((adamwSmallStepKernel<false, BFO_ROUND_SR>), grid, block, 0, stream, P, G, M, m, v, S, sv,
+                           gVec, pgVec, fl, ntiles, maxNorm, out, s, skip, k0, k1);
+    else
+        hipLaunchKernelGGL((adamwSmallStepKernel<false, BFO_ROUND_RNE>), grid, block, 0, stream, P, G, M, m, v, S,
+                           sv, gVec, pgVec, fl, ntiles, maxNorm, out, s, skip, k0, k1);
+    return hipGetLastError();
+}
+
 hipError_t launchCursorAdvance(uint64_t *cursor, hipStream_t stream) {
     hipLaunchKernelGGL(cursorAdvanceKernel, dim3(1), dim3(64), 0, stream, cursor);
     return hipGetLastError();
@@ -973,13 +1056,17 @@ hipError_t launchOutlierReset(OutlierState *state, uint32_t window, hipStream_t 
 }
 
 hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
-                              uint64_t seed, hipStream_t stream) {
+                              uint64_t seed, int rounding, hipStream_t stream) {
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
     const uint64_t tiles = (S + kTileElems - 1) / kTileElems;
     for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
-        hipLaunchKernelGGL(masterToBf16Kernel, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P, S, sv, pgVec,
-                           k0, k1, base);
+        if (rounding == BFO_ROUND_SR)
+            hipLaunchKernelGGL(masterToBf16Kernel<BFO_ROUND_SR>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P,
+                               S, sv, pgVec, k0, k1, base);
+        else
+            hipLaunchKernelGGL(masterToBf16Kernel<BFO_ROUND_RNE>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M,
+                               P, S, sv, pgVec, k0, k1, base);
     }
     return hipGetLastError();
 }

@@ -260,35 +260,20 @@ int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, floa
                   float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
                   uint64_t seed, int rounding, void *stream);
 
-/* One AdamW step over the shard ("04 · 多 GPU 与混合精度" §2.2, with the
- * lerp computed as two fused multiply-adds; "第 13 讲" §1.7 for bias
- * correction and decoupled decay).  Per element i (global) / j (local):
- *   g   = scale * f32(grads[j])
- *   m1  = fma(b1, m[j], fma(-b1, g, g));  v1 = fma(b2, v[j], fma(-b2, g*g, g*g))
- *   mh  = m1 / bc1;  vh = v1 / bc2;  u = mh / (sqrt(vh) + eps)
- *   old = master ? master[j] : f32(params[j])
- *   p   = old - lr * (u + w_i * old),  w_i = weight_decay if i's tensor has
- *         BFO_FLAG_DECAY else 0
- *   m[j] = m1; v[j] = v1; master[j] = p (when master != NULL);
- *   params[j] = SR(p, r16(i, seed)) or RNE(p)
- * each a single binary32 operation in that order.  bc1/bc2 =
- * (float)(1 - pow(beta, t)) in binary64, or 1 when bias correction is off.
- * SR rounds to the next bf16 away from zero when the 16 discarded bits of p
- * exceed r16, else truncates; r16 is a 16-bit draw of Philox4x32-10 (Salmon
- * et al., SC'11) with counter (lo32(i>>3), hi32(i>>3), 0, 0) and key
- * (lo32(seed), hi32(seed)); element i takes output word (i>>1)&3, low half
- * for even i.  RNE rounds to nearest, ties to even.  NaN stays NaN.
- * i is element j's global index (its run's global + offset), so every
- * layout and shard count draws the same r16 for the same parameter.
- * master == NULL selects the no-master path (old weights read from params).
- * scale: device float (e.g. &out->scale of grad_global_norm), or NULL for 1.
- * skip: device int32 (e.g. written by bfo_outlier_update), or NULL; when it
- * holds a nonzero value at run time the step changes nothing (every
- * workgroup exits after reading it).
- * t: 1-based step number (0 -> BFO_EINVAL).  rounding: BFO_ROUND_SR/RNE. */
-int adamw_sr_step(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
-                  float *v, const bfo_adamw_hparams *hp, const float *scale, const int32_t *skip, uint64_t t,
-                  uint64_t seed, int rounding, void *stream);
+/* grad_global_norm and then adamw_sr_step with that norm's clip scale, in
+ * one call ("04 · 多 GPU 与混合精度" §4 for the norm and clip, §2.2 for the
+ * update): the result -- *out, params, master, m, v -- is bit for bit that
+ * of the two calls.  For shards of at most 65,536 elements (8 norm tiles)
+ * both run in one kernel launch: every workgroup of the update forms the
+ * whole shard's sum of squares itself, in the norm's partition and order,
+ * so a small step pays one launch instead of two (workspace is then not
+ * used); larger shards take the two calls' launches.  skip: as in
+ * adamw_sr_step (the norm is still written).  Arguments and errors as the
+ * two calls; out and workspace must not overlap the arrays. */
+int adamw_sr_step_with_norm(bfo_table table, uint16_t *params, const uint16_t *grads, float *master, float *m,
+                            float *v, const bfo_adamw_hparams *hp, float max_norm, void *workspace,
+                            bfo_norm_result *out, const int32_t *skip, uint64_t t, uint64_t seed, int rounding,
+                            void *stream);
 
 /* The per-step scalars of adamw_sr_step, for a step whose launches are
  * recorded once (HIP graph capture) and replayed every step: they are read
@@ -336,6 +321,12 @@ int bfo_cursor_advance(uint64_t *cursor, void *stream);
  * bf16 output bit for bit. */
 int master_to_bf16_sr(bfo_table table, const float *master, uint16_t *params, uint64_t seed,
                       void *stream);
+
+/* The same rebuild with a rounding mode: BFO_ROUND_SR as master_to_bf16_sr,
+ * BFO_ROUND_RNE params = RNE(master[j]) (seed unused), which reproduces an
+ * update made with round-to-nearest.  Unknown rounding: BFO_EINVAL. */
+int master_to_bf16(bfo_table table, const float *master, uint16_t *params, uint64_t seed, int rounding,
+                   void *stream);
 
 /* Test export: out[k] = r16(first + k, seed) for k < count (device array,
  * 2-byte aligned).  Any first and count. */
@@ -405,37 +396,63 @@ int bfo_outlier_update(bfo_outlier detector, const float *value, float *z, int32
 
 /* Checkpoints ("04 · 多 GPU 与混合精度" §5.1-5.2).  Each rank saves its own
  * optimizer state; a DONE marker written after every rank has saved makes
- * the checkpoint count; resume takes the newest step with a marker.  The
- * bf16 weights are not saved when there is a master: after loading, call
- * master_to_bf16_sr(table, master, params, seed) with the returned seed and
- * they come back bit-identical to the ones the saved step produced.
+ * the checkpoint count; resume takes the newest step with a marker.  With a
+ * master, the bf16 weights need not be saved: loading rebuilds them from the
+ * master with the saved seed and rounding mode, bit-identical to the ones
+ * the saved step produced, and because only the master is needed the same
+ * state can also resume a run without a master (the page's precision switch
+ * at resume).
  *
- * bfo_checkpoint_save writes <dir>/state_<step:08>_<rank:05>.bin: a 96-byte
- * header (magic "BFOSTATE", version 1, step, seed, n, S, world, rank,
- * layout, whether a master is stored, and a fingerprint of the tensor table)
- * and the payload master (S fp32) -- or, when master is NULL, the shard's
- * bf16 params in shard-local order (params addressed as in adamw_sr_step) --
- * then m and v (S fp32 each).  step is the last step the state includes and
- * seed the rounding seed of its update.  Device arrays are copied through a
- * pinned buffer on `stream` after the work already queued there; the call
- * returns when the file is on disk (written under a temporary name, synced,
- * then renamed).  Errors: BFO_EINVAL, BFO_EIO, BFO_EHIP. */
+ * bfo_checkpoint_save writes <dir>/state_<step:08>_<rank:05>.bin: a 128-byte
+ * header (magic "BFOSTATE", version 2, step, seed, n, S, world, rank,
+ * layout, whether a master and whether params are stored, a fingerprint of
+ * the tensor table, the rounding mode, a checksum of each payload array and
+ * one of the header) and the payload: master (S fp32) when master is not
+ * NULL, the shard's bf16 params in shard-local order when params is not NULL
+ * (params addressed as in adamw_sr_step), then m and v (S fp32 each).  At
+ * least one of master and params must be given.  step is the last step the
+ * state includes; seed and rounding (BFO_ROUND_SR / BFO_ROUND_RNE) are those
+ * of the last update that changed the state.  Pass params too when that
+ * update is not known for sure -- e.g. when a device skip flag may have
+ * dropped it: the stored params are then restored as they are.  The
+ * checksums are bfo_checksum64 of each array's bytes as stored.  Device
+ * arrays are copied through a pinned buffer on `stream` after the work
+ * already queued there; the call returns when the file is on disk (written
+ * under a temporary name, synced, renamed into place, directory synced).
+ * Errors: BFO_EINVAL, BFO_EIO, BFO_EHIP. */
 int bfo_checkpoint_save(const char *dir, bfo_table table, const uint16_t *params, const float *master,
-                        const float *m, const float *v, uint64_t step, uint64_t seed, void *stream);
+                        const float *m, const float *v, uint64_t step, uint64_t seed, int rounding, void *stream);
 
-/* Creates the empty marker <dir>/DONE_<step:08>. */
+/* Creates the empty marker <dir>/DONE_<step:08> and syncs it and the
+ * directory to disk. */
 int bfo_checkpoint_done(const char *dir, uint64_t step);
 
 /* *step = the largest step with a DONE marker in dir; BFO_ENOTFOUND if none. */
 int bfo_checkpoint_latest(const char *dir, uint64_t *step);
 
-/* Reads this rank's state of `step` into master (or, when master is NULL,
- * into the shard's positions of params), m and v; *seed (if not NULL) gets
- * the saved seed.  BFO_ENOTFOUND if the file is missing; BFO_EFORMAT if its
- * header does not match the table (sizes, world, rank, layout, fingerprint,
- * master or not) or the file is truncated. */
+/* Reads this rank's state of `step`; *seed (if not NULL) gets the saved seed.
+ * m and v are always read.  master not NULL: the stored master is read into
+ * it (BFO_EFORMAT if the file has none).  params not NULL: the shard's
+ * positions of params get the stored params if the file has them, else they
+ * are rebuilt from the stored master as master_to_bf16 does with the saved
+ * seed and rounding mode -- also when master is NULL, which resumes a
+ * master checkpoint in a run without one (v's buffer then holds the master
+ * while the params are rebuilt, before v is read).  master and params may
+ * not both be NULL.  BFO_ENOTFOUND if the file is missing; BFO_EFORMAT if
+ * its header does not match the table (sizes, world, rank, layout,
+ * fingerprint), the file is truncated, or a checksum does not match (the
+ * arrays then hold partly loaded data and must not be used). */
 int bfo_checkpoint_load(const char *dir, uint64_t step, bfo_table table, uint16_t *params, float *master,
                         float *m, float *v, uint64_t *seed, void *stream);
+
+/* The 64-bit checksum stored in checkpoint headers, of `bytes` bytes of host
+ * memory: four lanes h[0..3] (h[l] starting at the 64-bit FNV-1a offset
+ * basis + l) take the data in 32-byte blocks (the last one padded with
+ * zeros), lane l folding the block's l-th little-endian 8-byte word w in as
+ * h[l] = (h[l] ^ w) * 1099511628211; then x = basis ^ bytes and, for each
+ * lane in order, x = (x ^ h[l]) * 1099511628211, x ^= x >> 29.  A change
+ * that stays within one 8-byte word always changes the result.  Host only. */
+uint64_t bfo_checksum64(const void *data, uint64_t bytes);
 
 /* Placement of the step's arrays in device memory (a measured property of
  * MI355X, not of the method).  The update streams five arrays at the same

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -177,8 +178,41 @@ def test_checkpoint_latest_reads_done_markers(bfo, tmp_path):
     assert lib.bfo_checkpoint_latest(os.fsencode(str(tmp_path / "missing")), ctypes.byref(ctypes.c_uint64())) == bfo.EIO
     assert lib.bfo_checkpoint_latest(None, None) == bfo.EINVAL
     assert lib.bfo_checkpoint_done(None, 1) == bfo.EINVAL
-    assert lib.bfo_checkpoint_save(b"/tmp", None, None, None, None, None, 1, 1, None) == bfo.EINVAL
+    assert lib.bfo_checkpoint_save(b"/tmp", None, None, None, None, None, 1, 1, 0, None) == bfo.EINVAL
     assert lib.bfo_checkpoint_load(b"/tmp", 1, None, None, None, None, None, None, None) == bfo.EINVAL
+
+
+def _checksum_by_definition(data):
+    """The checksum as bf16opt.h defines it, step by step in Python integers."""
+    mask = (1 << 64) - 1
+    prime, basis = 1099511628211, 14695981039346656037
+    lanes = [basis + l for l in range(4)]
+    padded = bytes(data) + b"\0" * (-len(data) % 32)
+    for blk in range(0, len(padded), 32):
+        for l in range(4):
+            w = int.from_bytes(padded[blk + 8 * l:blk + 8 * l + 8], "little")
+            lanes[l] = ((lanes[l] ^ w) * prime) & mask
+    x = basis ^ len(data)
+    for h in lanes:
+        x = ((x ^ h) * prime) & mask
+        x ^= x >> 29
+    return x
+
+
+def test_checksum64_follows_its_definition_and_sees_every_flipped_byte(bfo):
+    rs = np.random.default_rng(9)
+    for n in (0, 1, 7, 8, 31, 32, 33, 100, 1000):
+        data = rs.integers(0, 256, n, dtype=np.uint8).tobytes()
+        assert bfo.checksum64(data) == _checksum_by_definition(data), n
+    data = bytearray(rs.integers(0, 256, 4096 + 5, dtype=np.uint8).tobytes())
+    base = bfo.checksum64(data)
+    for pos in range(len(data)):                      # every single-byte change is seen
+        for flip in (0x01, 0x80):
+            data[pos] ^= flip
+            assert bfo.checksum64(data) != base, pos
+            data[pos] ^= flip
+    # appending zero bytes changes the length, hence the sum
+    assert bfo.checksum64(bytes(data) + b"\0") != base
 
 
 def test_spread_layout_puts_each_array_on_its_own_16_gib_boundary(bfo):

@@ -361,6 +361,78 @@ def test_update_gpt2_124m_all_ten_steps(bfo):
     chk.close()
 
 
+def _one_call_case(bfo, w, world, rank, layout, master, rounding, steps=3, nan_at=None):
+    """The same steps through grad_global_norm + adamw_sr_step and through
+    adamw_sr_step_with_norm, on copies of one state: identical bits."""
+    T = bfo.Table(w.entries(), world, rank, layout=layout)
+    n_pg = T.pg_size
+    P0, _, _, _ = W.init_state(torch, w, 0, n_pg, DEV, master=False)
+    a = {"P": P0, "M": (torch.randn(T.size, device=DEV) * 0.02) if master else None,
+         "m": torch.zeros(T.size, device=DEV), "v": torch.zeros(T.size, device=DEV)}
+    b = {k: (None if t is None else t.clone()) for k, t in a.items()}
+    G = torch.empty(n_pg, dtype=torch.bfloat16, device=DEV)
+    ra, rb = bfo.new_norm_result(DEV), bfo.new_norm_result(DEV)
+    ws = bfo.new_norm_workspace(T)
+    for t in range(1, steps + 1):
+        W.fill_grads(torch, w, G, 0, t)
+        if nan_at is not None and t == steps:
+            G[nan_at] = float("nan")
+        bfo.grad_global_norm(T, G, ra, w.hparams.max_norm)
+        bfo.adamw_sr_step(T, a["P"], G, a["M"], a["m"], a["v"], w.hparams, t, step_seed(t), scale=ra,
+                          rounding=rounding)
+        bfo.adamw_sr_step_with_norm(T, b["P"], G, b["M"], b["m"], b["v"], w.hparams, t, step_seed(t), rb,
+                                    w.hparams.max_norm, rounding=rounding, workspace=ws)
+        assert ra.cpu().numpy().tobytes() == rb.cpu().numpy().tobytes(), ("norm", t)
+    for k in ("P", "M", "m", "v"):
+        if a[k] is not None:
+            x, y = host_copy({k: a[k]})[k], host_copy({k: b[k]})[k]
+            assert _same_bits(x, y), (k, w.name, world, rank, layout, master, rounding)
+    return bfo.read_norm_result(rb)
+
+
+@pytest.mark.parametrize("master,rounding", [(True, o.ROUND_SR), (False, o.ROUND_RNE)])
+@pytest.mark.parametrize("case", ["tiny", "tiny_per_tensor", "tiny_misaligned", "ragged", "eight_tiles",
+                                  "nine_tiles", "five"])
+def test_one_call_step_equals_the_two_calls(bfo, case, master, rounding):
+    # One launch for shards of at most 8 norm tiles (65,536 elements), the
+    # two calls' launches above; every bit of the norm and the state equal.
+    cases = {
+        "tiny": (W.tiny(), 1, 0, bfo.LAYOUT_FLAT),
+        "tiny_per_tensor": (W.tiny(), 2, 1, bfo.LAYOUT_PER_TENSOR),
+        "tiny_misaligned": (padded_tiny(4), 4, 1, bfo.LAYOUT_FLAT),
+        "ragged": (ragged_workload(3, 13), 1, 0, bfo.LAYOUT_FLAT),
+        "eight_tiles": (W.Workload("e", [("a", (1000, 60)), ("b", (5536,))], grad_std=0.3), 1, 0,
+                        bfo.LAYOUT_FLAT),
+        "nine_tiles": (W.Workload("n", [("a", (1000, 60)), ("b", (5537,))], grad_std=0.3), 1, 0,
+                       bfo.LAYOUT_FLAT),
+        "five": (W.Workload("f", [("a", (5,))], grad_std=0.3), 1, 0, bfo.LAYOUT_FLAT),
+    }
+    w, world, rank, layout = cases[case]
+    _one_call_case(bfo, w, world, rank, layout, master, rounding)
+
+
+def test_one_call_step_skip_and_non_finite(bfo):
+    w = W.tiny()
+    got = _one_call_case(bfo, w, 1, 0, bfo.LAYOUT_FLAT, True, o.ROUND_SR, nan_at=77)
+    assert math.isnan(got[1])
+    T = bfo.Table(w.entries())
+    st = device_state(w, 0, w.n, DEV)
+    W.fill_grads(torch, w, st["G"], 0, 1)
+    before = host_copy(st)
+    res = bfo.new_norm_result(DEV)
+    skip = torch.ones(1, dtype=torch.int32, device=DEV)
+    bfo.adamw_sr_step_with_norm(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, 1, step_seed(1), res,
+                                skip=skip)
+    after = host_copy(st)
+    for k in ("P", "M", "m", "v"):
+        assert _same_bits(before[k], after[k]), k
+    assert_norm_parity(bfo.read_norm_result(res), o.grad_norm(before["G"], 1.0))      # the norm is still written
+    with pytest.raises(bfo.BfoError) as e:                    # out inside m
+        bfo.adamw_sr_step_with_norm(T, st["P"], st["G"], st["M"], st["m"], st["v"], w.hparams, 1, 1,
+                                    st["m"][8:12].view(torch.float64))
+    assert e.value.status == bfo.EINVAL
+
+
 def test_update_is_deterministic(bfo):
     w = ragged_workload(40, 3)
     T = bfo.Table(w.entries())
@@ -1086,46 +1158,195 @@ def test_step_control_pipeline_skips_the_spike(bfo):
 # --------------------------------------------------------------------- checkpoint / resume
 
 
-def test_checkpoint_resume_is_bit_exact(bfo, tmp_path):
-    # "04 · 多 GPU 与混合精度" §5.2: resume from (master, m, v, last seed),
-    # rebuild the bf16 weights with the last update's draws, and the run
-    # continues bit-identically to one that never stopped.
-    w = ragged_workload(6, 3)
-    w.grad_std = 0.05
-    T = bfo.Table(w.entries())
-    st = device_state(w, 0, w.n, DEV)
-    res = bfo.new_norm_result(DEV)
+def _same_bits(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
 
-    def step(state, t):
-        W.fill_grads(torch, w, state["G"], 0, t)
-        bfo.grad_global_norm(T, state["G"], res)
-        bfo.adamw_sr_step(T, state["P"], state["G"], state["M"], state["m"], state["v"], w.hparams, t,
-                          step_seed(t), scale=res)
 
-    for t in range(1, 5):
-        step(st, t)
-    P4 = st["P"].clone()
+class _Run:
+    """A GPU run of the ragged workload beside the oracle's own run of it:
+    both start from the same state and take the same grads; the oracle is
+    fed the GPU's clip scale (norms compared separately)."""
+
+    def __init__(self, bfo, master=True, rounding=o.ROUND_SR):
+        self.bfo = bfo
+        self.w = ragged_workload(6, 3)
+        self.w.grad_std = 0.05
+        self.T = bfo.Table(self.w.entries())
+        self.tbl = o.table(self.w.entries())
+        self.st = device_state(self.w, 0, self.w.n, DEV, master=master)
+        self.h = host_copy(self.st)
+        self.res = bfo.new_norm_result(DEV)
+        self.rounding = rounding
+
+    def gpu_step(self, state, t, skip=None, rounding=None):
+        rounding = self.rounding if rounding is None else rounding
+        W.fill_grads(torch, self.w, state["G"], 0, t)
+        self.bfo.grad_global_norm(self.T, state["G"], self.res)
+        self.bfo.adamw_sr_step(self.T, state["P"], state["G"], state.get("M"), state["m"], state["v"],
+                               self.w.hparams, t, step_seed(t), scale=self.res, rounding=rounding, skip=skip)
+        got = self.bfo.read_norm_result(self.res)
+        return got[2]
+
+    def both_step(self, t):
+        scale = self.gpu_step(self.st, t)
+        self.h["G"] = u16(self.st["G"])
+        assert_norm_parity(self.bfo.read_norm_result(self.res), o.grad_norm(self.h["G"], 1.0))
+        oracle_step(self.tbl, 0, self.h, self.w.hparams, scale, t, step_seed(t), self.rounding)
+        return scale
+
+    def fresh(self, master=True):
+        return {"P": torch.empty_like(self.st["P"]),
+                "M": torch.empty(self.w.n, dtype=torch.float32, device=DEV) if master else None,
+                "m": torch.empty_like(self.st["m"]), "v": torch.empty_like(self.st["v"]),
+                "G": torch.empty_like(self.st["G"])}
+
+
+def test_checkpoint_resume_matches_the_oracle(bfo, tmp_path):
+    # "04 · 多 GPU 与混合精度" §5.1-5.2: save (master, m, v, last seed) at
+    # step 4 -- not the bf16 weights --, resume in fresh buffers (the load
+    # rebuilds the params from the master with the saved draws), run to step
+    # 8.  The oracle runs steps 1-8 from the same start: the rebuilt params
+    # equal its step-4 params and the resumed run its step-8 state, bit for
+    # bit, as does the run that never stopped.
+    run = _Run(bfo)
     d = str(tmp_path)
-    bfo.checkpoint_save(d, T, st["m"], st["v"], 4, step_seed(4), master=st["M"])
-    assert bfo.checkpoint_latest(d) is None            # not done until marked
-    bfo.checkpoint_done(d, 4)
-    for t in range(5, 9):
-        step(st, t)
-    want = host_copy(st)
+    scales = {}
+    for t in range(1, 9):
+        scales[t] = run.both_step(t)
+        if t == 4:
+            bfo.checkpoint_save(d, run.T, run.st["m"], run.st["v"], 4, step_seed(4), master=run.st["M"])
+            assert bfo.checkpoint_latest(d) is None            # not done until marked
+            bfo.checkpoint_done(d, 4)
+            at4 = {k: (None if a is None else a.copy()) for k, a in run.h.items()}
+    uninterrupted = host_copy(run.st)
+    for k in ("P", "M", "m", "v"):
+        assert _same_bits(uninterrupted[k], run.h[k]), f"uninterrupted run vs oracle: {k}"
 
-    fresh = {"P": torch.empty_like(st["P"]), "M": torch.empty_like(st["M"]), "m": torch.empty_like(st["m"]),
-             "v": torch.empty_like(st["v"]), "G": torch.empty_like(st["G"])}
+    fresh = run.fresh()
     last = bfo.checkpoint_latest(d)
     assert last == 4
-    seed = bfo.checkpoint_load(d, last, T, fresh["m"], fresh["v"], master=fresh["M"])
-    assert seed == step_seed(4)
-    bfo.master_to_bf16_sr(T, fresh["M"], fresh["P"], seed)
-    assert torch.equal(fresh["P"].view(torch.int16), P4.view(torch.int16))
-    for t in range(5, 9):
-        step(fresh, t)
+    assert bfo.checkpoint_load(d, last, run.T, fresh["m"], fresh["v"], master=fresh["M"],
+                               params=fresh["P"]) == step_seed(4)
     got = host_copy(fresh)
     for k in ("P", "M", "m", "v"):
-        assert np.array_equal(got[k].view(np.uint8), want[k].view(np.uint8)), k
+        assert _same_bits(got[k], at4[k]), f"loaded step-4 {k} vs oracle"
+    for t in range(5, 9):
+        assert run.gpu_step(fresh, t) == scales[t]
+    got = host_copy(fresh)
+    for k in ("P", "M", "m", "v"):
+        assert _same_bits(got[k], run.h[k]), f"resumed step-8 {k} vs oracle"
+
+
+@pytest.mark.parametrize("stored_params", [False, True])
+def test_checkpoint_resumes_a_run_without_master(bfo, tmp_path, stored_params):
+    # "04 · 多 GPU 与混合精度" §5.2: only the fp32 master is needed, so the
+    # same state can resume under another precision setup.  A master run
+    # saves at step 4; a run without a master loads it (params rebuilt by SR
+    # with the saved seed, the master staged in v's buffer -- or the stored
+    # params taken as they are) and goes on with the no-master update.  The
+    # oracle does the same from its own step-4 state.
+    run = _Run(bfo)
+    d = str(tmp_path)
+    for t in range(1, 5):
+        run.both_step(t)
+    bfo.checkpoint_save(d, run.T, run.st["m"], run.st["v"], 4, step_seed(4), master=run.st["M"],
+                        params=run.st["P"] if stored_params else None)
+    bfo.checkpoint_done(d, 4)
+    fresh = run.fresh(master=False)
+    fresh["P"].view(torch.int16).fill_(0x7FA5)
+    fresh["v"].fill_(float("nan"))
+    assert bfo.checkpoint_load(d, 4, run.T, fresh["m"], fresh["v"], params=fresh["P"]) == step_seed(4)
+    got = host_copy(fresh)
+    for k in ("P", "m", "v"):
+        assert _same_bits(got[k], run.h[k]), f"step-4 {k} vs oracle"
+    oracle_h = {k: (None if k == "M" else a) for k, a in run.h.items()}
+    for t in range(5, 9):
+        scale = run.gpu_step(fresh, t)
+        oracle_h["G"] = u16(fresh["G"])
+        oracle_step(run.tbl, 0, oracle_h, run.w.hparams, scale, t, step_seed(t), o.ROUND_SR)
+    got = host_copy(fresh)
+    for k in ("P", "m", "v"):
+        assert _same_bits(got[k], oracle_h[k]), f"no-master step-8 {k} vs oracle"
+
+
+def test_checkpoint_round_to_nearest_master_run(bfo, tmp_path):
+    # A master run that writes its bf16 weights by round-to-nearest: the
+    # header keeps the mode, and the load rebuilds the params as RNE(master),
+    # the oracle's step-3 params; master_to_bf16 with RNE does the same, and
+    # an SR rebuild of the same master would not.
+    run = _Run(bfo, rounding=o.ROUND_RNE)
+    d = str(tmp_path)
+    for t in range(1, 4):
+        run.both_step(t)
+    bfo.checkpoint_save(d, run.T, run.st["m"], run.st["v"], 3, step_seed(3), master=run.st["M"],
+                        rounding=bfo.ROUND_RNE)
+    fresh = run.fresh()
+    bfo.checkpoint_load(d, 3, run.T, fresh["m"], fresh["v"], master=fresh["M"], params=fresh["P"])
+    assert _same_bits(u16(fresh["P"]), run.h["P"])
+    assert _same_bits(o.round_nearest_even(run.h["M"]), run.h["P"])
+    P2 = torch.empty_like(fresh["P"])
+    bfo.master_to_bf16(run.T, fresh["M"], P2, 0, bfo.ROUND_RNE)
+    assert _same_bits(u16(P2), run.h["P"])
+    bfo.master_to_bf16(run.T, fresh["M"], P2, step_seed(3), bfo.ROUND_SR)
+    assert not _same_bits(u16(P2), run.h["P"])
+    with pytest.raises(bfo.BfoError) as e:
+        bfo.master_to_bf16(run.T, fresh["M"], P2, 0, 7)
+    assert e.value.status == bfo.EINVAL
+
+
+def test_checkpoint_after_a_skipped_update_keeps_the_stored_params(bfo, tmp_path):
+    # A step whose update a device flag skipped leaves the step-3 state, but
+    # the caller, which does not wait for the flag, saves "step 4, seed 4".
+    # With the params stored, the load restores them as they are (the
+    # oracle's step-3 params); a rebuild with seed 4 would not give them.
+    run = _Run(bfo)
+    d = str(tmp_path)
+    for t in range(1, 4):
+        run.both_step(t)
+    skip = torch.ones(1, dtype=torch.int32, device=DEV)
+    run.gpu_step(run.st, 4, skip=skip)
+    assert _same_bits(u16(run.st["P"]), run.h["P"]) and _same_bits(f32(run.st["M"]), run.h["M"])
+    bfo.checkpoint_save(d, run.T, run.st["m"], run.st["v"], 4, step_seed(4), master=run.st["M"],
+                        params=run.st["P"])
+    fresh = run.fresh()
+    bfo.checkpoint_load(d, 4, run.T, fresh["m"], fresh["v"], master=fresh["M"], params=fresh["P"])
+    got = host_copy(fresh)
+    for k in ("P", "M", "m", "v"):
+        assert _same_bits(got[k], run.h[k]), k
+    rebuilt = o.master_to_bf16_sr(run.h["M"], 0, step_seed(4))
+    assert not _same_bits(rebuilt, run.h["P"])
+
+
+def test_checkpoint_refuses_a_corrupted_file(bfo, tmp_path):
+    # One flipped byte anywhere in the payload, or in the header, is refused
+    # (BFO_EFORMAT) by the per-array and header checksums; the intact file
+    # loads.
+    run = _Run(bfo)
+    for t in (1, 2):
+        run.both_step(t)
+    d = str(tmp_path)
+    bfo.checkpoint_save(d, run.T, run.st["m"], run.st["v"], 2, step_seed(2), master=run.st["M"],
+                        params=run.st["P"])
+    path = tmp_path / "state_00000002_00000.bin"
+    data = bytearray(path.read_bytes())
+    n = run.w.n
+    header = 128
+    assert len(data) == header + (4 + 2 + 4 + 4) * n
+    offsets = {"header (seed)": 24, "master": header + 4 * 17 + 1, "params": header + 4 * n + 2 * 5,
+               "m": header + 6 * n + 4 * (n - 1) + 3, "v": header + 10 * n + 4 * (n // 2)}
+    fresh = run.fresh()
+    for what, pos in offsets.items():
+        data[pos] ^= 0x10
+        path.write_bytes(bytes(data))
+        with pytest.raises(bfo.BfoError) as e:
+            bfo.checkpoint_load(d, 2, run.T, fresh["m"], fresh["v"], master=fresh["M"], params=fresh["P"])
+        assert e.value.status == bfo.EFORMAT, what
+        data[pos] ^= 0x10
+    path.write_bytes(bytes(data))
+    bfo.checkpoint_load(d, 2, run.T, fresh["m"], fresh["v"], master=fresh["M"], params=fresh["P"])
+    got = host_copy(fresh)
+    for k in ("P", "M", "m", "v"):
+        assert _same_bits(got[k], run.h[k]), k
 
 
 def test_checkpoint_no_master_per_tensor_round_trip_and_errors(bfo, tmp_path):
