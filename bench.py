@@ -186,19 +186,27 @@ def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs, norm
     14 written with a master, 12 and 10 without -- in its vector and
     workgroup plan, no arithmetic; key 0 leaves m, v and the master
     unchanged), timed per launch with HIP events on the launch stream, as the
-    update is.  With `norm` (enqueues the real grad norm of grads[k]) it also
-    times K steps of norm + stream mix over the same grads, back to back like
-    the timed region: the step's own ceiling."""
-    for _ in range(2):
-        bfo.stream_mix(P, G, M, m, v, 0)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
-    for a, z in evs:
-        a.record(stream)
-        bfo.stream_mix(P, G, M, m, v, 0)
-        z.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(z) for a, z in evs) / launches
-    per = UPDATE_BYTES if M is not None else UPDATE_BYTES_NO_MASTER
+    update is.  Then the same reads alone and the same writes alone (which
+    overwrite the state, so they run last): `serial_bound` is the rate the
+    mix would reach if HBM served its reads and its writes one after the
+    other at those rates.  With `norm` (enqueues the real grad norm of
+    grads[k]) it also times K steps of norm + stream mix over the same grads,
+    back to back like the timed region: the step's own ceiling."""
+    def per_launch(mode):
+        for _ in range(2):
+            bfo.stream_mix(P, G, M, m, v, 0, mode)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        for a, z in evs:
+            a.record(stream)
+            bfo.stream_mix(P, G, M, m, v, 0, mode)
+            z.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(z) for a, z in evs) / launches
+
+    ms = per_launch(bfo.MIX_BOTH)
+    rd_b, wr_b = (14, 14) if M is not None else (12, 10)
+    per = rd_b + wr_b
     gbs = per * m.numel() / (ms * 1e-3) / 1e9
     out = {"kernel": "streamMixKernel (update traffic, no arithmetic)", "achieved": round(gbs, 1),
            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms, 5),
@@ -216,6 +224,15 @@ def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs, norm
         step_ms = a.elapsed_time(z) / launches
         out["step_ms"] = round(step_ms, 5)
         out["step_over_ceiling"] = round(step_ms / ms_step, 4)
+    ms_r = per_launch(bfo.MIX_READS)
+    ms_w = per_launch(bfo.MIX_WRITES)          # overwrites m, v, the master and the params
+    r_gbs = rd_b * m.numel() / (ms_r * 1e-3) / 1e9
+    w_gbs = wr_b * m.numel() / (ms_w * 1e-3) / 1e9
+    bound = per / (rd_b / r_gbs + wr_b / w_gbs)
+    out["reads_only"] = {"GBps": round(r_gbs, 1), "frac": round(r_gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms_r, 5)}
+    out["writes_only"] = {"GBps": round(w_gbs, 1), "frac": round(w_gbs / HBM_PEAK_GBS, 4), "ms_avg": round(ms_w, 5)}
+    out["serial_bound"] = {"GBps": round(bound, 1), "frac": round(bound / HBM_PEAK_GBS, 4),
+                           "mix_over_bound": round(gbs / bound, 4), "update_over_bound": round(update_gbs / bound, 4)}
     return out
 
 

@@ -124,7 +124,7 @@ def _lib():
         "master_to_bf16_sr": (i32, [vp, vp, vp, u64, vp]),
         "bfo_rng_dump": (i32, [u64, u64, u64, vp, vp]),
         "bfo_decay_mask_dump": (i32, [vp, vp, vp]),
-        "bfo_stream_mix": (i32, [vp, vp, vp, vp, vp, u64, u32, vp]),
+        "bfo_stream_mix": (i32, [vp, vp, vp, vp, vp, u64, u32, i32, vp]),
         "bfo_plan_runs": (i32, [ctypes.POINTER(BfoTensor), u32, u32, u32, i32, ctypes.POINTER(BfoRun), u32,
                                 ctypes.POINTER(u32), pu64]),
         "bfo_step_scalars_fill": (i32, [ctypes.POINTER(AdamwHParams), u64, ctypes.c_float, u64,
@@ -555,18 +555,23 @@ def decay_mask_dump(table):
     return out
 
 
-def stream_mix(params, grads, master, m, v, key=0):
+MIX_BOTH, MIX_READS, MIX_WRITES = 0, 1, 2
+
+
+def stream_mix(params, grads, master, m, v, key=0, mode=MIX_BOTH):
     """The update's memory traffic without its arithmetic (bandwidth ceiling).
 
-    With a master: m, v, master ^= key as bit patterns and params = grads ^
-    (key & 0xFFFF).  master None: m, v ^= key and params ^= grads ^ (key & 0xFFFF)."""
+    MIX_BOTH with a master: m, v, master ^= key as bit patterns and params =
+    grads ^ (key & 0xFFFF); master None: m, v ^= key and params ^= grads ^
+    (key & 0xFFFF).  MIX_READS: the same reads, nothing written.  MIX_WRITES:
+    the same writes (key- and index-made words), nothing read."""
     count = m.numel()
     dev = m.device
     args = [_arg(params, torch.bfloat16, count, "params", dev), _arg(grads, torch.bfloat16, count, "grads", dev),
             _arg(master, torch.float32, count, "master", dev), _arg(m, torch.float32, count, "m", dev),
             _arg(v, torch.float32, count, "v", dev)]
     with torch.cuda.device(dev):
-        _check("bfo_stream_mix", _lib().bfo_stream_mix(*args, count, key & 0xFFFFFFFF, _stream(dev)))
+        _check("bfo_stream_mix", _lib().bfo_stream_mix(*args, count, key & 0xFFFFFFFF, mode, _stream(dev)))
 
 
 def checkpoint_save(directory, table, m, v, step, seed, master=None, params=None, rounding=ROUND_SR):

@@ -583,13 +583,15 @@ int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream) {
 }
 
 int bfo_stream_mix(uint16_t *params, const uint16_t *grads, float *master, float *m, float *v, uint64_t count,
-                   uint32_t key, void *stream) {
+                   uint32_t key, int mode, void *stream) {
+    if (mode != BFO_MIX_BOTH && mode != BFO_MIX_READS && mode != BFO_MIX_WRITES) return BFO_EINVAL;
     if (count == 0) return BFO_OK;
     if (!params || !grads || !m || !v) return BFO_EINVAL;
     if (!alignedTo(params, 16) || !alignedTo(grads, 16) || !alignedTo(master, 16) || !alignedTo(m, 16) ||
         !alignedTo(v, 16))
         return BFO_EMISALIGNED;
-    hipError_t he = bfo::launchStreamMix(params, grads, master, m, v, count, key, static_cast<hipStream_t>(stream));
+    hipError_t he =
+        bfo::launchStreamMix(params, grads, master, m, v, count, key, mode, static_cast<hipStream_t>(stream));
     return he == hipSuccess ? BFO_OK : hipFail(he);
 }
 

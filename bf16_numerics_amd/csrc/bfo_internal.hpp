@@ -130,7 +130,7 @@ hipError_t launchRngDump(uint64_t first, uint64_t count, uint64_t seed, uint16_t
                          hipStream_t stream);
 hipError_t launchDecayDump(ShardView sv, uint64_t S, uint8_t *out, hipStream_t stream);
 hipError_t launchStreamMix(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t count,
-                           uint32_t key, hipStream_t stream);
+                           uint32_t key, int mode, hipStream_t stream);
 
 // Outlier detector state in device memory: a ring of the last `window`
 // finite values (oldest at `head` once full).

@@ -395,18 +395,28 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
 // ---------------------------------------------------------------------------
 // Measurement kernel: the update's memory traffic without its arithmetic.
 // Same tile, lane and vector plan as the 16-byte path of adamwTileKernel
-// (with a master: reads G, m, v, M and writes m, v, M, P; without: reads G,
-// P, m, v and writes P, m, v), each output a bit-XOR of its inputs and a key,
-// so that nothing can be elided; key 0 leaves m, v and M bitwise as they
-// were.  The same cache policies as the update: nontemporal grads loads and,
-// with a master, nontemporal params stores.  Its bandwidth is the ceiling
-// the update can reach on a given device.
+// and the same cache policies (nontemporal grads loads and, with a master,
+// nontemporal params stores).  kMode:
+//   BFO_MIX_BOTH: the update's reads and writes (with a master: reads G, m,
+//     v, M and writes m, v, M, P; without: reads G, P, m, v and writes P, m,
+//     v), each output a bit-XOR of its inputs and the key, so nothing can be
+//     elided; key 0 leaves m, v and M bitwise as they were;
+//   BFO_MIX_READS: the update's reads alone; the loaded words are folded
+//     into one 64-bit value per lane, which is compared with a constant: on
+//     a match (odds 2^-64 per lane) the lane stores the m vector it loaded
+//     back unchanged, so the loads stay and no state changes;
+//   BFO_MIX_WRITES: the update's writes alone, of words made from the key
+//     and the element index (m, v, M and P are overwritten).
+// BOTH is the ceiling of the update's own mix; READS and WRITES time its two
+// directions on their own, for the bound the mix would have if HBM served
+// reads and writes one after the other.
 // ---------------------------------------------------------------------------
-template <bool kMaster>
+template <bool kMaster, int kMode>
 __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__ P, const uint16_t *__restrict__ G,
                                                           float *__restrict__ M, float *__restrict__ Mom,
                                                           float *__restrict__ Var, uint64_t count, uint32_t key,
                                                           uint64_t tileBase) {
+    constexpr bool kRead = kMode != BFO_MIX_WRITES;
     const uint64_t tile = tileBase + blockIdx.x;
     uint4 gv[kVecPerLane], pv[kVecPerLane], ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
     uint4 wa[kVecPerLane], wb[kVecPerLane];
@@ -415,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
     for (int k = 0; k < kVecPerLane; ++k) {
         const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
         mode[k] = q * 8 + 8 <= count ? kRegular : (q * 8 < count ? kPerElement : kNone);
-        if (mode[k] != kRegular) continue;
+        if (mode[k] != kRegular || !kRead) continue;
         gv[k] = loadOnce16(G, q);
         ma[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q];
         mb[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q + 1];
@@ -428,11 +438,24 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
             pv[k] = reinterpret_cast<const uint4 *>(P)[q];
         }
     }
+    if constexpr (kMode == BFO_MIX_READS) {
+#pragma unroll
+        for (int k = 0; k < kVecPerLane; ++k) {
+            if (mode[k] != kRegular) continue;
+            uint4 x = gv[k] ^ ma[k] ^ mb[k] ^ va[k] ^ vb[k];
+            if constexpr (kMaster) x = x ^ wa[k] ^ wb[k];
+            else x = x ^ pv[k];
+            const uint64_t folded = (uint64_t(x.x ^ x.z) << 32) | uint64_t(x.y ^ x.w);
+            const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+            if (folded == (0x9E3779B97F4A7C15ull ^ key)) reinterpret_cast<uint4 *>(Mom)[2 * q] = ma[k];
+        }
+        return;
+    }
     const uint32_t key2 = (key & 0xFFFFu) | (key << 16);
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
         const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-        if (mode[k] == kPerElement) {
+        if (mode[k] == kPerElement && kMode == BFO_MIX_BOTH) {
             for (uint64_t j = q * 8; j < count; ++j) {
                 Mom[j] = __uint_as_float(__float_as_uint(Mom[j]) ^ key);
                 Var[j] = __uint_as_float(__float_as_uint(Var[j]) ^ key);
@@ -445,7 +468,28 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
             }
             continue;
         }
+        if (mode[k] == kPerElement) {
+            for (uint64_t j = q * 8; j < count; ++j) {
+                const uint32_t x = key ^ uint32_t(j);
+                Mom[j] = __uint_as_float(x);
+                Var[j] = __uint_as_float(x ^ 1u);
+                if constexpr (kMaster) M[j] = __uint_as_float(x ^ 2u);
+                P[j] = uint16_t(x);
+            }
+            continue;
+        }
         if (mode[k] != kRegular) continue;
+        if constexpr (kMode == BFO_MIX_WRITES) {
+            const uint32_t x = key ^ uint32_t(q * 8);
+            ma[k] = make_uint4(x, x + 1, x + 2, x + 3);
+            mb[k] = make_uint4(x + 4, x + 5, x + 6, x + 7);
+            va[k] = ma[k] ^ make_uint4(1u, 1u, 1u, 1u);
+            vb[k] = mb[k] ^ make_uint4(1u, 1u, 1u, 1u);
+            wa[k] = ma[k] ^ make_uint4(2u, 2u, 2u, 2u);
+            wb[k] = mb[k] ^ make_uint4(2u, 2u, 2u, 2u);
+            gv[k] = make_uint4(x, x ^ 3u, x ^ 5u, x ^ 7u);
+            pv[k] = make_uint4(0u, 0u, 0u, 0u);
+        }
         const uint4 kk = make_uint4(key, key, key, key);
         const uint4 k2 = make_uint4(key2, key2, key2, key2);
         reinterpret_cast<uint4 *>(Mom)[2 * q] = ma[k] ^ kk;
@@ -1071,17 +1115,27 @@ hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView
     return hipGetLastError();
 }
 
-hipError_t launchStreamMix(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t count,
-                           uint32_t key, hipStream_t stream) {
+template <bool kMaster, int kMode>
+void launchStreamMixT(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t count, uint32_t key,
+                      hipStream_t stream) {
     const uint64_t tiles = (count + kTileElems - 1) / kTileElems;
     for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
-        if (M)
-            hipLaunchKernelGGL(streamMixKernel<true>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m, v,
-                               count, key, base);
-        else
-            hipLaunchKernelGGL(streamMixKernel<false>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m, v,
-                               count, key, base);
+        hipLaunchKernelGGL((streamMixKernel<kMaster, kMode>), dim3(uint32_t(nb)), dim3(kBlock), 0, stream, P, G, M, m,
+                           v, count, key, base);
+    }
+}
+
+hipError_t launchStreamMix(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t count,
+                           uint32_t key, int mode, hipStream_t stream) {
+    if (M) {
+        if (mode == BFO_MIX_READS) launchStreamMixT<true, BFO_MIX_READS>(P, G, M, m, v, count, key, stream);
+        else if (mode == BFO_MIX_WRITES) launchStreamMixT<true, BFO_MIX_WRITES>(P, G, M, m, v, count, key, stream);
+        else launchStreamMixT<true, BFO_MIX_BOTH>(P, G, M, m, v, count, key, stream);
+    } else {
+        if (mode == BFO_MIX_READS) launchStreamMixT<false, BFO_MIX_READS>(P, G, M, m, v, count, key, stream);
+        else if (mode == BFO_MIX_WRITES) launchStreamMixT<false, BFO_MIX_WRITES>(P, G, M, m, v, count, key, stream);
+        else launchStreamMixT<false, BFO_MIX_BOTH>(P, G, M, m, v, count, key, stream);
     }
     return hipGetLastError();
 }

@@ -338,17 +338,25 @@ int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
 
 /* Measurement export: the update's memory traffic with none of its
  * arithmetic, for an achievable-bandwidth ceiling measured the same way as
- * the update.  For j < count (device arrays of count elements):
- *   with a master: m[j], v[j], master[j] ^= key (as 32-bit patterns) and
- *     params[j] = grads[j] ^ (key & 0xFFFF) -- 14 bytes read and 14 written
- *     per element, as the master update;
- *   master == NULL: m[j], v[j] ^= key and params[j] ^= grads[j] ^
- *     (key & 0xFFFF) -- 12 read and 10 written, as the no-master update;
- * in the update's 16-byte vector and workgroup plan.  key 0 leaves m, v and
- * master unchanged.  Every non-null pointer 16-byte aligned (else
- * BFO_EMISALIGNED); count 0 is a no-op. */
+ * the update, in the update's 16-byte vector and workgroup plan and with its
+ * cache policies.  For j < count (device arrays of count elements):
+ *   BFO_MIX_BOTH -- with a master: m[j], v[j], master[j] ^= key (as 32-bit
+ *     patterns) and params[j] = grads[j] ^ (key & 0xFFFF): 14 bytes read and
+ *     14 written per element, as the master update; master == NULL: m[j],
+ *     v[j] ^= key and params[j] ^= grads[j] ^ (key & 0xFFFF): 12 read and 10
+ *     written, as the no-master update.  key 0 leaves m, v and master
+ *     unchanged;
+ *   BFO_MIX_READS -- the same reads and no writes (14 or 12 bytes per
+ *     element); nothing changes;
+ *   BFO_MIX_WRITES -- the same writes and no reads (14 or 10 bytes per
+ *     element) of words made from key and j: m, v, master and params are
+ *     overwritten.
+ * READS and WRITES time the two directions of the mix on their own.  Every
+ * non-null pointer 16-byte aligned (else BFO_EMISALIGNED); unknown mode
+ * BFO_EINVAL; count 0 is a no-op. */
+enum { BFO_MIX_BOTH = 0, BFO_MIX_READS = 1, BFO_MIX_WRITES = 2 };
 int bfo_stream_mix(uint16_t *params, const uint16_t *grads, float *master, float *m, float *v, uint64_t count,
-                   uint32_t key, void *stream);
+                   uint32_t key, int mode, void *stream);
 
 /* Learning-rate schedules ("04 · 多 GPU 与混合精度" §4 names cosine, linear,
  * constant and wsd; the formulas are this library's reading).  For 0-based

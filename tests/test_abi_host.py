@@ -103,10 +103,11 @@ def test_entry_points_reject_null_table_and_bad_scalars(bfo):
     assert lib.bfo_rng_dump(0, 10, 0, None, None) == bfo.EINVAL
     assert lib.bfo_rng_dump(0, 10, 0, ctypes.c_void_p(1), None) == bfo.EMISALIGNED
     assert lib.bfo_rng_dump(2**64 - 5, 10, 0, ctypes.c_void_p(16), None) == bfo.ERANGE
-    assert lib.bfo_stream_mix(None, None, None, None, None, 0, 0, None) == bfo.OK
-    assert lib.bfo_stream_mix(None, None, None, None, None, 8, 0, None) == bfo.EINVAL
+    assert lib.bfo_stream_mix(None, None, None, None, None, 0, 0, 0, None) == bfo.OK
+    assert lib.bfo_stream_mix(None, None, None, None, None, 8, 0, 0, None) == bfo.EINVAL
+    assert lib.bfo_stream_mix(None, None, None, None, None, 0, 0, 3, None) == bfo.EINVAL
     p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(24)
-    assert lib.bfo_stream_mix(p16, p16, p16, p16, p8, 8, 0, None) == bfo.EMISALIGNED
+    assert lib.bfo_stream_mix(p16, p16, p16, p16, p8, 8, 0, 0, None) == bfo.EMISALIGNED
     st = bfo.StepScalars()
     assert lib.bfo_step_scalars_fill(ctypes.byref(hp), 0, 1e-3, 1, ctypes.byref(st)) == bfo.EINVAL
     assert lib.bfo_step_scalars_fill(None, 1, 1e-3, 1, ctypes.byref(st)) == bfo.EINVAL

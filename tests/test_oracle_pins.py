@@ -281,6 +281,38 @@ def test_norm_brute_force_exact_and_extremes():
     assert o.grad_norm(np.array([0x3F80], np.uint16), 1.0)[2] == 1.0
 
 
+def _round_to_f32(fr):
+    """The binary32 value nearest the exact rational fr (ties to even)."""
+    x = np.float32(float(fr))
+    best = None
+    for c in (np.nextafter(x, np.float32(-np.inf)), x, np.nextafter(x, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - fr)
+        if best is None or d < best[0] or (d == best[0] and int(np.array(c).view(np.uint32)) & 1 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_bias_corrections_equal_the_exact_values_rounded_once():
+    # "第 13 讲" §1.7: the corrections are 1 - beta1^t and 1 - beta2^t.  With
+    # beta the binary32 hyperparameter, the exact rational 1 - beta^t rounded
+    # once to binary32 must be what the oracle uses (it forms beta^t in
+    # binary64 with pow, so this also pins it against libm), t = 1..300 and
+    # 500, 1000, 2000, 5000, for three (beta1, beta2) pairs.
+    for b1, b2 in ((0.9, 0.95), (0.9, 0.999), (0.8, 0.99)):
+        f1, f2 = np.float32(b1), np.float32(b2)
+        e1, e2 = Fraction(float(f1)), Fraction(float(f2))
+        p1 = p2 = Fraction(1)
+        wanted = set(range(1, 301)) | {500, 1000, 2000, 5000}
+        for t in range(1, 5001):
+            p1 *= e1
+            p2 *= e2
+            if t in wanted:
+                bc1, bc2 = o.bias_corrections(f1, f2, t, True)
+                assert np.float32(bc1) == _round_to_f32(1 - p1), (b1, t)
+                assert np.float32(bc2) == _round_to_f32(1 - p2), (b2, t)
+    assert o.bias_corrections(np.float32(0.9), np.float32(0.95), 7, False) == (1.0, 1.0)
+
+
 def test_norm_from_sumsq_closed_forms():
     # The root and the clip scale alone: sum of squares 16 -> norm 4, scale
     # 1/4 (max 1) or 1/2 (max 2); 1/4 -> 1/2, not clipped; a norm equal to
