@@ -197,6 +197,29 @@ __device__ __forceinline__ void placeElement(const ShardView &sv, uint32_t &k, u
     rng = sv.rng[k] + off;
 }
 
+// Tile words for a workgroup of a partition shifted by `shift` vectors
+// (0..7): workgroup t takes vectors [t*kTileVecs - shift, (t+1)*kTileVecs -
+// shift), which lie in the plan's tiles t-1 and t.  The rebuild shifts a
+// flat shard whose bf16 params start 32, 64 or 96 bytes into a 128-byte
+// line so that every wave's 1 KiB of params stores starts on a line (the
+// fp32 master, 32 bytes per vector, then starts on a 64-byte boundary).
+// Measured on the 1.5B model's shards, one process, against the unshifted
+// partition: rebuild +0.8% (rank 1), +2.2% (rank 2), +1.5% (rank 3), equal
+// on rank 0; the update loses 0.5-0.8% with the same shift (its master, m
+// and v are 12 of its 14 bytes written), so it keeps the plain partition.
+struct TileWords {
+    uint32_t before, at;  // plan words of tiles t-1 (when shifted) and t
+    __device__ __forceinline__ uint32_t of(uint64_t q, uint64_t t) const { return q < t * kTileVecs ? before : at; }
+};
+
+__device__ __forceinline__ TileWords tileWords(const ShardView &sv, uint64_t t, uint32_t shift, uint64_t S) {
+    const uint64_t planTiles = (S + kTileElems - 1) / kTileElems;
+    TileWords w;
+    w.at = t < planTiles ? sv.tile[t] : 0u;
+    w.before = (shift && t) ? sv.tile[t - 1] : w.at;
+    return w;
+}
+
 // ---------------------------------------------------------------------------
 // One element of the AdamW step.  `w` is the element's decay (wd or 0),
 // `old` the fp32 weight before the step; returns the new fp32 weight.
@@ -516,18 +539,19 @@ template <int kRound>
 __global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
                                                              uint16_t *__restrict__ P, uint64_t S,
                                                              ShardView sv, int pgVec, uint32_t key0,
-                                                             uint32_t key1, uint64_t tileBase) {
+                                                             uint32_t key1, uint64_t tileBase, uint32_t shift) {
     const uint64_t tile = tileBase + blockIdx.x;
-    const uint32_t tileWord = sv.tile[tile];
+    const TileWords tw = tileWords(sv, tile, shift, S);
     F32x4 a[kVecPerLane], b[kVecPerLane];
     Place pl[kVecPerLane];
     int mode[kVecPerLane];
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
-        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t u = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t q = u - shift;
         mode[k] = kNone;
-        if (q * 8 >= S) continue;
-        pl[k] = placeVector(sv, tileWord, q * 8, S);
+        if (u < shift || q * 8 >= S) continue;
+        pl[k] = placeVector(sv, tw.of(q, tile), q * 8, S);
         if (!pl[k].inRun) {
             mode[k] = kPerElement;
             continue;
@@ -539,7 +563,7 @@ __global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__rest
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
         if (mode[k] == kNone) continue;
-        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x - shift;
         if (mode[k] == kPerElement) {
             uint32_t run = pl[k].run;
             uint64_t cachedGroup = UINT64_MAX;
@@ -980,6 +1004,16 @@ __global__ __launch_bounds__(64) void outlierResetKernel(OutlierState *st, uint3
     st->pad = 0;
 }
 
+// The rebuild's partition shift (in 8-element vectors) that puts every
+// wave's params stores on a 128-byte line: flat shards with 16-byte-aligned
+// params that start an even number of 16-byte units into a line (an odd
+// number would leave the master 32 bytes off a 64-byte boundary: no shift).
+uint32_t lineShift(const uint16_t *P, const ShardView &sv, int pgVec) {
+    if (sv.flatBegin == UINT64_MAX || !pgVec) return 0;
+    const uint32_t units = uint32_t(reinterpret_cast<uintptr_t>(P) >> 4) & 7u;
+    return (units & 1u) ? 0u : units;
+}
+
 template <bool kMaster, int kRound, bool kScheduled>
 hipError_t launchAdamwT(uint16_t *P, const uint16_t *G, float *M, float *m, float *v, uint64_t S,
                         ShardView sv, int pgVec, StepScalars s, const float *scale, const int32_t *skip,
@@ -1102,15 +1136,16 @@ hipError_t launchOutlierReset(OutlierState *state, uint32_t window, hipStream_t 
 hipError_t launchMasterToBf16(const float *M, uint16_t *P, uint64_t S, ShardView sv, int pgVec,
                               uint64_t seed, int rounding, hipStream_t stream) {
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
-    const uint64_t tiles = (S + kTileElems - 1) / kTileElems;
+    const uint32_t shift = lineShift(P, sv, pgVec);
+    const uint64_t tiles = ((S + 7) / 8 + shift + kTileVecs - 1) / kTileVecs;
     for (uint64_t base = 0; base < tiles; base += kMaxBlocksPerLaunch) {
         const uint64_t nb = tiles - base < kMaxBlocksPerLaunch ? tiles - base : kMaxBlocksPerLaunch;
         if (rounding == BFO_ROUND_SR)
             hipLaunchKernelGGL(masterToBf16Kernel<BFO_ROUND_SR>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M, P,
-                               S, sv, pgVec, k0, k1, base);
+                               S, sv, pgVec, k0, k1, base, shift);
         else
             hipLaunchKernelGGL(masterToBf16Kernel<BFO_ROUND_RNE>, dim3(uint32_t(nb)), dim3(kBlock), 0, stream, M,
-                               P, S, sv, pgVec, k0, k1, base);
+                               P, S, sv, pgVec, k0, k1, base, shift);
     }
     return hipGetLastError();
 }
