@@ -37,18 +37,29 @@ def kernel_source_digest():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per update launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_record(workload):
+    """The committed counter summary of a workload, if it was taken on the
+    current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"adamw_update_{workload}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
-        return None
-    return rec.get("bytes_per_launch")
+    return rec if rec.get("kernel_source_sha256_16") == kernel_source_digest() else None
+
+
+def measured_traffic(workload):
+    """HBM bytes per update launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    rec = traffic_record(workload)
+    return rec.get("bytes_per_launch") if rec else None
+
+
+def measured_rebuild_traffic(workload):
+    """HBM bytes per rebuild launch from the same summary, or None."""
+    rec = traffic_record(workload)
+    return (rec.get("rebuild") or {}).get("bytes_per_launch") if rec else None
 
 
 def cpu_model():
@@ -561,6 +572,7 @@ def main():
         del src, dst
     if M is not None:
         out["rebuild"] = rebuild_rate(torch, bfo, stream, T, M, P, last_seed, args.steps)
+        out["rebuild"]["traffic"] = measured_rebuild_traffic(w.name) if default_variant else None
     if not args.no_cpu_baseline and args.layout == "flat":
         st = {"P": P, "G": pool[0], "M": M, "m": m, "v": v}
         out["cpu_baseline"] = cpu_baseline(torch, w, st, b, args.cpu_seconds, args.rounding == "sr")

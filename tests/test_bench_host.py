@@ -84,3 +84,12 @@ def test_committed_counter_records_are_consistent(path):
         np.mean(rec["update_FETCH_SIZE_KiB"]) * 1024 * rec["fetch_scale"], rel=1e-6)
     assert rec["write_bytes_per_launch"] == pytest.approx(
         np.mean(rec["update_WRITE_SIZE_KiB"]) * 1024 * rec["write_scale"], rel=1e-6)
+    # the rebuild (6 B per element) and the three no-math probes (28, 14, 14 B)
+    for part, per in [(rec["rebuild"], 6)] + [(rec["stream_mix"][k], b) for k, b in
+                                              (("both", 28), ("reads_only", 14), ("writes_only", 14))]:
+        assert part["algorithmic_bytes_per_launch"] == per * rec["shard_elems"]
+        assert part["bytes_per_launch"] == pytest.approx(part["read_bytes_per_launch"] + part["write_bytes_per_launch"],
+                                                         abs=2)
+        assert part["over_algorithmic"] == pytest.approx(part["bytes_per_launch"] / part["algorithmic_bytes_per_launch"],
+                                                         abs=1e-5)
+        assert 0.999 <= part["over_algorithmic"] < 1.03
