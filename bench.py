@@ -204,10 +204,15 @@ def stream_ceiling(torch, bfo, stream, P, G, M, m, v, launches, update_gbs, norm
     grads[k]) it also times K steps of norm + stream mix over the same grads,
     back to back like the timed region: the step's own ceiling."""
     def per_launch(mode):
-        for _ in range(2):
-            bfo.stream_mix(P, G, M, m, v, 0, mode)
+        # events recorded once beforehand and two untimed launches ahead, so
+        # that the host is ahead of the GPU when the timed intervals start
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(launches)]
+        for a, z in evs:
+            a.record(stream)
+            z.record(stream)
+        for _ in range(2):
+            bfo.stream_mix(P, G, M, m, v, 0, mode)
         for a, z in evs:
             a.record(stream)
             bfo.stream_mix(P, G, M, m, v, 0, mode)

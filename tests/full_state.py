@@ -112,14 +112,26 @@ class FullStateChecker:
         return sum(self.pool.map(lambda r: o.grad_norm(G_host_u16[r[0]:r[1]], self.max_norm)[0],
                                  parts(G_host_u16.size, self.k)))
 
-    def oracle_step_host(self, h, begin, scale, t, seed, rounding):
+    def oracle_step_host(self, h, begin, scale, t, seed, rounding, segments=None, offset=0):
         """The oracle step in place over host arrays h (numpy; P, G uint16; M, m,
-        v float32) for global elements [begin, begin + len(h["P"]))."""
-        sl = (lambda a, r: None if a is None else a[r[0]:r[1]])
-        list(self.pool.map(lambda r: o.adamw_step(self.tbl, begin + r[0], sl(h["P"], r), sl(h["G"], r),
-                                                  sl(h.get("M"), r), sl(h["m"], r), sl(h["v"], r), self.hp,
-                                                  scale, t, seed, rounding),
-                           parts(h["P"].size, self.k)))
+        v float32).  Element j holds global index begin + j; or, with
+        `segments` [(local_lo, local_hi, global_lo), ...] covering the shard,
+        shard element offset + j lies in the segment that holds it, at global
+        index global_lo + (offset + j - local_lo)."""
+        n = h["P"].size
+        jobs = []
+        for a, b in parts(n, self.k):
+            if segments is None:
+                jobs.append((a, b, begin + a))
+                continue
+            for lo, hi, g in segments:
+                x, y = max(a, lo - offset), min(b, hi - offset)
+                if x < y:
+                    jobs.append((x, y, g + (offset + x - lo)))
+        sl = (lambda arr, j: None if arr is None else arr[j[0]:j[1]])
+        list(self.pool.map(lambda j: o.adamw_step(self.tbl, j[2], sl(h["P"], j), sl(h["G"], j), sl(h.get("M"), j),
+                                                  sl(h["m"], j), sl(h["v"], j), self.hp, scale, t, seed, rounding),
+                           jobs))
 
     def compare_host_to_device(self, got, ref, what):
         """Compare device state `got` (P int16/bf16, M, m, v) with host numpy
@@ -148,9 +160,11 @@ class FullStateChecker:
     def _add(a, b):
         return {k: a.get(k, 0) + b.get(k, 0) for k in set(a) | set(b)}
 
-    def check_step(self, pre, post, G, begin, scale, t, seed, rounding):
+    def check_step(self, pre, post, G, begin, scale, t, seed, rounding, segments=None):
         """Oracle(pre, G, scale) against the GPU's post-state over every element.
-        Returns (diff counts per array, oracle sum of squares of G)."""
+        All arrays shard-local; element j is global index begin + j, or as
+        `segments` map it (see oracle_step_host).  Returns (diff counts per
+        array, oracle sum of squares of G)."""
         S = post["m"].numel()
         counts = {k: 0 for k in self.d}
         sumsq = 0.0
@@ -163,7 +177,7 @@ class FullStateChecker:
                 self.h[k][:n].copy_(src.view(torch.int16) if k == "P" else src)
             h = {k: self._np(k, n) for k in self.h}
             sumsq += self.oracle_norm_parts(h["G"])
-            self.oracle_step_host(h, begin + lo, scale, t, seed, rounding)
+            self.oracle_step_host(h, begin + lo, scale, t, seed, rounding, segments, lo)
             for k in self.d:
                 self.d[k][:n].copy_(self.h[k][:n])
             counts = self._add(counts, self._compare_chunk(post, lo, hi, f"t={t} [{lo},{hi})"))

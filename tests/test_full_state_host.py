@@ -117,3 +117,38 @@ def test_compare_nan_positions():
     z[0] = 0x3F80 - 0x8000                                         # sign flipped
     with pytest.raises(AssertionError):
         compare_bf16(x, z, "sign")
+
+
+def test_checker_segments_follow_a_per_tensor_shard():
+    # A per-tensor shard (rank 1 of 2 of the d=32 model): shard elements map to
+    # runs of global indices; the checker, told the runs, gives the oracle's
+    # own mapped step over the whole shard, chunked across run boundaries.
+    w = W.tiny()
+    tbl = o.table(w.entries())
+    hp = o.hparams(w.hparams.lr, w.hparams.beta1, w.hparams.beta2, w.hparams.eps, w.hparams.weight_decay)
+    rc, gidx = o.shard_map_per_tensor(tbl, 2, 1)
+    assert rc == o.OK
+    S = gidx.size
+    segs, lo = [], 0
+    for j in range(1, S + 1):
+        if j == S or gidx[j] != gidx[j - 1] + 1:
+            segs.append((lo, j, int(gidx[lo])))
+            lo = j
+    pre, G = _state(S, 3)
+    rs = np.random.default_rng(4)
+    P_full = rs.integers(0, 1 << 16, w.n, dtype=np.uint64).astype(np.uint16)
+    G_full = rs.integers(0, 1 << 16, w.n, dtype=np.uint64).astype(np.uint16) & 0x3FFF   # finite, small
+    P_full[gidx] = pre["P"].view(torch.int16).numpy().view(np.uint16)
+    G_full[gidx] = G.view(torch.int16).numpy().view(np.uint16)
+    h = {"M": pre["M"].numpy().copy(), "m": pre["m"].numpy().copy(), "v": pre["v"].numpy().copy()}
+    o.adamw_step_mapped(tbl, gidx, P_full, G_full, h["M"], h["m"], h["v"], hp, 0.7, 2, 99)
+    post = {"P": torch.from_numpy(P_full[gidx].view(np.int16)).view(torch.bfloat16),
+            "M": torch.from_numpy(h["M"]), "m": torch.from_numpy(h["m"]), "v": torch.from_numpy(h["v"])}
+    chk = FullStateChecker(tbl, hp, 1.0, True, "cpu", chunk=1000, threads=3)
+    counts, _ = chk.check_step(pre, post, G, 0, 0.7, 2, 99, o.ROUND_SR, segments=segs)
+    assert all(c == 0 for c in counts.values()), counts
+    # without the segments (as if the shard were contiguous from 0) the decay
+    # flags and draws differ: refused
+    with pytest.raises(AssertionError):
+        chk.check_step(pre, post, G, 0, 0.7, 2, 99, o.ROUND_SR)
+    chk.close()

@@ -880,10 +880,11 @@ def test_full_size_gpt2_1p5b_eight_shards_equal_the_unsharded_step(bfo):
 
 def per_tensor_full_size(bfo, w, world, rank, steps=2):
     """llm.c's ZeRO-1 layout at full size: rank `rank` of `world` owns 1/world
-    of every tensor; P and G are the full n-element buffers.  The oracle
-    steps sampled windows of the shard (around every run start, the ends and
-    random places) through the global index map; the norm is compared over
-    the whole shard."""
+    of every tensor; P and G are the full n-element buffers.  Every shard
+    element of P, M, m and v is compared with the oracle after each step
+    (gathered to shard order on the device, the oracle stepping each run of
+    consecutive global indices), the norm over the whole shard, and every
+    params position outside the shard must keep its bits."""
     ents = w.entries()
     tbl = o.table(ents)
     T = bfo.Table(ents, world, rank, layout=bfo.LAYOUT_PER_TENSOR)
@@ -893,31 +894,31 @@ def per_tensor_full_size(bfo, w, world, rank, steps=2):
     P, M_full, m0, v0 = W.init_state(torch, w, 0, w.n, DEV)
     del m0, v0
     gi = torch.from_numpy(gidx.astype(np.int64)).to(DEV)
+    del gidx
     st = {"M": M_full[gi].clone(), "m": torch.zeros(S, device=DEV), "v": torch.zeros(S, device=DEV)}
-    del M_full, gi
+    del M_full
     torch.cuda.empty_cache()
     G = torch.empty(w.n, dtype=torch.bfloat16, device=DEV)
     res = bfo.new_norm_result(DEV)
-    wins = windows([(local, 0, 0) for local, *_ in T.runs()], 0, S, seed=3)
+    segs = [(local, local + length, glob) for local, _addr, glob, length, _flags in T.runs()]
+    chk = FullStateChecker(tbl, oracle_hparams(w.hparams), w.hparams.max_norm, True, DEV)
     for t in range(1, steps + 1):
         W.fill_grads(torch, w, G, 0, t)
-        Ph, Gh = u16(P), u16(G)
-        pre = [{k: f32(st[k][lo:hi]) for k in ("M", "m", "v")} for lo, hi in wins]
+        P_before = P.clone()
+        pre = {"P": P[gi], "M": st["M"].clone(), "m": st["m"].clone(), "v": st["v"].clone()}
+        G_loc = G[gi]
         bfo.grad_global_norm(T, G, res, w.hparams.max_norm)
         bfo.adamw_sr_step(T, P, G, st["M"], st["m"], st["v"], w.hparams, t, step_seed(t), scale=res)
         got = bfo.read_norm_result(res)
-        assert_norm_parity(got, o.grad_norm(np.ascontiguousarray(Gh[gidx]), w.hparams.max_norm))
-        for (lo, hi), h in zip(wins, pre):
-            g = gidx[lo:hi]
-            o.adamw_step_mapped(tbl, g, Ph, Gh, h["M"], h["m"], h["v"], oracle_hparams(w.hparams), got[2], t,
-                                step_seed(t))
-            gpu = u16(P[torch.from_numpy(g.astype(np.int64)).to(DEV)])
-            assert_bf16_parity(gpu, Ph[g], f"per-tensor {w.name} [{lo},{hi}) t={t} params")
-            for k in ("M", "m", "v"):
-                assert_f32_parity(f32(st[k][lo:hi]), h[k], f"per-tensor {w.name} [{lo},{hi}) t={t} {k}")
-        del Ph, Gh
-        print(f"{w.name} per-tensor rank {rank} of {world}, t={t}: norm {got[1]:.6f} scale {got[2]:.6f}, "
-              f"{len(wins)} windows", flush=True)
+        post = {"P": P[gi], "M": st["M"], "m": st["m"], "v": st["v"]}
+        counts, sumsq = chk.check_step(pre, post, G_loc, 0, got[2], t, step_seed(t), o.ROUND_SR, segments=segs)
+        assert_norm_parity(got, (sumsq, *o.norm_from_sumsq(sumsq, w.hparams.max_norm)))
+        report(f"{w.name} per-tensor rank {rank}/{world} t={t}", assert_counts(counts, S, f"per-tensor t={t}"))
+        P_before[gi] = post["P"]
+        assert torch.equal(P_before.view(torch.int16), P.view(torch.int16)), "a write escaped the shard"
+        del pre, post, G_loc, P_before
+        torch.cuda.empty_cache()
+    chk.close()
 
 
 def test_full_size_gpt2_1p5b_per_tensor(bfo):
