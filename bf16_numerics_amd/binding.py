@@ -387,7 +387,12 @@ def adamw_sr_step_with_norm(table, params, grads, master, m, v, hp, t, seed, out
     if out.dtype != torch.float64 or out.numel() != 2 or out.device != dev:
         raise ValueError("out must be new_norm_result(device)")
     sk = _arg(skip, torch.int32, 1, "skip", dev) if skip is not None else None
-    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws = None
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous() or \
+                workspace.numel() * workspace.element_size() < norm_workspace_bytes(table):
+            raise ValueError("workspace must be new_norm_workspace(table)")
+        ws = ctypes.c_void_p(workspace.data_ptr())
     with torch.cuda.device(dev):
         _check("adamw_sr_step_with_norm", _lib().adamw_sr_step_with_norm(
             table.handle, p, g, M, mm, vv, ctypes.byref(_hparams(hp)), max_norm, ws,

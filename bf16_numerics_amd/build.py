@@ -21,6 +21,7 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    "-pthread",
     "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",

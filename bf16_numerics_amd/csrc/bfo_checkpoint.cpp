@@ -36,6 +36,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "bfo_internal.hpp"
@@ -125,6 +126,29 @@ class Checksum {
     size_t pending_ = 0;
 };
 
+// Adds one chunk to a checksum on a helper thread, so that the sum of a
+// staged chunk overlaps the file write (or the device copy and the next
+// read) of the same bytes.  Chunks are added strictly in order: a chunk's
+// task is joined before the next one starts.
+class SumTask {
+  public:
+    ~SumTask() { join(); }
+    void start(Checksum &sum, const char *p, size_t n) {
+        join();
+        try {
+            th_ = std::thread([&sum, p, n] { sum.add(p, n); });
+        } catch (...) {
+            sum.add(p, n);  // no thread to be had: sum on this one
+        }
+    }
+    void join() {
+        if (th_.joinable()) th_.join();
+    }
+
+  private:
+    std::thread th_;
+};
+
 uint64_t headerSum(const Header &h) {
     Checksum c;
     c.add(&h, kHeaderSummed);
@@ -192,11 +216,14 @@ struct Stage {
             return (err = hipEventRecord(done[h], stream)) == hipSuccess;
         };
         if (chunks && !fetch(0)) return BFO_EHIP;
+        SumTask task;
         for (uint64_t k = 0; k < chunks; ++k) {
             const int h = int(k & 1);
             if ((err = hipEventSynchronize(done[h])) != hipSuccess) return BFO_EHIP;
+            // the other half is refilled only once its sum is done
+            task.join();
             if (k + 1 < chunks && !fetch(k + 1)) return BFO_EHIP;
-            sum.add(half(h), len(k));
+            task.start(sum, half(h), len(k));
             if (std::fwrite(half(h), 1, len(k), f) != len(k)) return BFO_EIO;
         }
         return BFO_OK;
@@ -208,6 +235,7 @@ struct Stage {
         const uint64_t chunks = (bytes + kHalf - 1) / kHalf;
         int rc = BFO_OK;
         bool pending[2] = {false, false};
+        SumTask task;
         for (uint64_t k = 0; k < chunks && rc == BFO_OK; ++k) {
             const int h = int(k & 1);
             const size_t n = size_t(bytes - k * kHalf < kHalf ? bytes - k * kHalf : kHalf);
@@ -216,11 +244,13 @@ struct Stage {
                 break;
             }
             pending[h] = false;
+            // half h was summed as chunk k-2; chunk k-1's sum must finish
+            // before chunk k's starts, and it overlaps this read
             if (std::fread(half(h), 1, n, f) != n) {
                 rc = BFO_EFORMAT;
                 break;
             }
-            sum.add(half(h), n);
+            task.start(sum, half(h), n);
             if ((err = hipMemcpyAsync(dst + k * kHalf, half(h), n, hipMemcpyHostToDevice, stream)) != hipSuccess ||
                 (err = hipEventRecord(done[h], stream)) != hipSuccess) {
                 rc = BFO_EHIP;
@@ -228,6 +258,7 @@ struct Stage {
             }
             pending[h] = true;
         }
+        task.join();
         // Both halves must be idle before the buffer can be freed or reused.
         const hipError_t e = hipStreamSynchronize(stream);
         if (rc == BFO_OK && e != hipSuccess) {

@@ -4,7 +4,9 @@ Each case draws a tensor table (tensors of 0-5,000 elements, random decay
 flags), a shard count and rank, a layout, master or no master, a rounding
 mode, and an element offset of 0-7 for the params and grads arrays (so their
 start is 2-byte aligned only, or any 16-byte phase), then runs the grad norm
-and two update steps on the GPU and the oracle on the same inputs.  Bars as
+and two update steps on the GPU (odd cases through the one-call step) and the
+oracle on the same inputs; with a master, the rebuild must give the last
+step's params back.  Bars as
 in the other parity tests: draws, maps and masks exact; bf16 params equal or
 one step apart in at most 1e-6 of the elements (none at these sizes); fp32
 state within relative 1e-6; norm within relative 1e-5.
@@ -93,8 +95,12 @@ def test_random_case_matches_the_oracle(bfo, k):
         G_all = (rs.normal(0, c["grad_std"], n).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
         g_src = G_all if c["layout"] == bfo.LAYOUT_PER_TENSOR else G_all[gidx.astype(np.int64)]
         dG.copy_(W.from_bf16_bits(torch, g_src, DEV))
-        bfo.grad_global_norm(T, dG, res, hp.max_norm)
-        bfo.adamw_sr_step(T, dP, dG, dM, dm, dv, hp, t, step_seed(t), scale=res, rounding=c["rounding"])
+        if k % 2:       # odd cases take the one-call step (one launch when S <= 65,536)
+            bfo.adamw_sr_step_with_norm(T, dP, dG, dM, dm, dv, hp, t, step_seed(t), res, hp.max_norm,
+                                        rounding=c["rounding"], workspace=bfo.new_norm_workspace(T))
+        else:
+            bfo.grad_global_norm(T, dG, res, hp.max_norm)
+            bfo.adamw_sr_step(T, dP, dG, dM, dm, dv, hp, t, step_seed(t), scale=res, rounding=c["rounding"])
         got = bfo.read_norm_result(res)
         assert_norm_parity(got, o.grad_norm(np.ascontiguousarray(G_all[gidx.astype(np.int64)]), hp.max_norm))
         o.adamw_step_mapped(tbl, gidx, h["P"], G_all, h["M"], h["m"], h["v"], oracle_hparams(hp), got[2], t,
@@ -106,5 +112,13 @@ def test_random_case_matches_the_oracle(bfo, k):
     assert np.array_equal(u16(buf_P[sh + pg_len:]), np.zeros(8 - sh, np.uint16)), "write past the params array"
     if M is not None:
         assert_f32_parity(f32(dM), h["M"], f"case {k} master")
+        # the rebuild from the master, in the step's rounding mode, gives the step's params back
+        P2 = dP.clone()
+        if c["layout"] == bfo.LAYOUT_PER_TENSOR:
+            P2.view(torch.int16)[torch.from_numpy(gidx.astype(np.int64)).to(DEV)] = 0x7FA5
+        else:
+            P2.view(torch.int16).fill_(0x7FA5)
+        bfo.master_to_bf16(T, dM, P2, step_seed(2), c["rounding"])
+        assert np.array_equal(u16(P2), gp), f"case {k} rebuild"
     assert_f32_parity(f32(dm), h["m"], f"case {k} m")
     assert_f32_parity(f32(dv), h["v"], f"case {k} v")
