@@ -181,6 +181,65 @@ int main(void) {
     printf("%s master_to_bf16_sr rebuilds the last step's bf16 params (GPU and oracle)\n", rb_ok ? "ok  " : "FAIL");
     failures += !rb_ok;
 
+    /* the allocation-free norm and the one-call step, on copies of the state:
+     * the same bits as grad_global_norm and as the two calls */
+    {
+        bfo_norm_result *dres2, *dres3;
+        uint16_t *dP2, *dP3;
+        float *dS2, *dS3;   /* master, m, v of each copy, each on a 16-byte boundary */
+        const uint64_t Sp = (S + 3) / 4 * 4;
+        HIP_OK(hipMalloc((void **)&dres2, sizeof(bfo_norm_result)));
+        HIP_OK(hipMalloc((void **)&dres3, sizeof(bfo_norm_result)));
+        HIP_OK(hipMalloc((void **)&dP2, n * 2));
+        HIP_OK(hipMalloc((void **)&dP3, n * 2));
+        HIP_OK(hipMalloc((void **)&dS2, 3 * Sp * 4));
+        HIP_OK(hipMalloc((void **)&dS3, 3 * Sp * 4));
+        HIP_OK(hipMemcpy(dP2, dP, n * 2, hipMemcpyDeviceToDevice));
+        HIP_OK(hipMemcpy(dP3, dP, n * 2, hipMemcpyDeviceToDevice));
+        const float *src[3] = {dM, dm, dv};
+        for (int a = 0; a < 3; ++a) {
+            HIP_OK(hipMemcpy(dS2 + a * Sp, src[a], S * 4, hipMemcpyDeviceToDevice));
+            HIP_OK(hipMemcpy(dS3 + a * Sp, src[a], S * 4, hipMemcpyDeviceToDevice));
+        }
+        BFO_OK_(grad_global_norm(tb, dG, 1.0f, dws, dres2, stream));
+        BFO_OK_(grad_global_norm_noalloc(tb, dG, 1.0f, dres3, stream));
+        bfo_norm_result r2, r3;
+        HIP_OK(hipMemcpyAsync(&r2, dres2, sizeof r2, hipMemcpyDeviceToHost, stream));
+        HIP_OK(hipMemcpyAsync(&r3, dres3, sizeof r3, hipMemcpyDeviceToHost, stream));
+        HIP_OK(hipStreamSynchronize(stream));
+        const int na_ok = memcmp(&r2, &r3, sizeof r2) == 0;
+        printf("%s grad_global_norm_noalloc gives grad_global_norm's bits\n", na_ok ? "ok  " : "FAIL");
+        failures += !na_ok;
+        const uint64_t t7 = 7, seed7 = (1337ull << 32) | 7;
+        BFO_OK_(adamw_sr_step(tb, dP2 + b, dG, dS2, dS2 + Sp, dS2 + 2 * Sp, &hp, &dres2->scale, NULL, t7, seed7,
+                              BFO_ROUND_SR, stream));
+        BFO_OK_(adamw_sr_step_with_norm(tb, dP3 + b, dG, dS3, dS3 + Sp, dS3 + 2 * Sp, &hp, 1.0f, dws, dres3, NULL,
+                                        t7, seed7, BFO_ROUND_SR, stream));
+        HIP_OK(hipStreamSynchronize(stream));
+        uint16_t *c2 = malloc(n * 2), *c3 = malloc(n * 2);
+        float *s2 = malloc(3 * Sp * 4), *s3 = malloc(3 * Sp * 4);
+        if (!c2 || !c3 || !s2 || !s3) return 1;
+        HIP_OK(hipMemcpy(c2, dP2, n * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(c3, dP3, n * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(s2, dS2, 3 * Sp * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(s3, dS3, 3 * Sp * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(&r3, dres3, sizeof r3, hipMemcpyDeviceToHost));
+        int state_same = 1;
+        for (int a = 0; a < 3; ++a) state_same &= memcmp(s2 + a * Sp, s3 + a * Sp, S * 4) == 0;
+        const int oc_ok = memcmp(c2, c3, n * 2) == 0 && state_same &&
+                          memcmp(&r2, &r3, sizeof r2) == 0 && memcmp(c2, gP, n * 2) != 0;
+        printf("%s adamw_sr_step_with_norm gives the two calls' bits (norm, params, master, m, v)\n",
+               oc_ok ? "ok  " : "FAIL");
+        failures += !oc_ok;
+        free(c2); free(c3); free(s2); free(s3);
+        HIP_OK(hipFree(dres2));
+        HIP_OK(hipFree(dres3));
+        HIP_OK(hipFree(dP2));
+        HIP_OK(hipFree(dP3));
+        HIP_OK(hipFree(dS2));
+        HIP_OK(hipFree(dS3));
+    }
+
     /* steps 4..6 from a graph: per-step scalars in device memory, a cursor */
     bfo_step_scalars hsteps[3];
     for (int k = 0; k < 3; ++k) BFO_OK_(bfo_step_scalars_fill(&hp, 4 + k, hp.lr, (1337ull << 32) | (4 + k), &hsteps[k]));

@@ -30,4 +30,4 @@ def test_step_from_c_matches_the_oracle_bit_for_bit(tmp_path):
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
-    assert r.stdout.count("ok  ") == 12
+    assert r.stdout.count("ok  ") == 14
