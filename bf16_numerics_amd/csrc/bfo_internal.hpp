@@ -11,11 +11,16 @@ namespace bfo {
 
 // One workgroup of the streaming kernels: 256 lanes = 4 wave64s.
 constexpr int kBlock = 256;
-// Each lane of the update / rebuild kernels owns kVecPerLane 8-element
-// vectors (16 bytes of bf16, 32 bytes of fp32 per vector and array).
+// Both kernels that step through the shard's tiles give a workgroup one
+// tile of kTileElems elements.  Each lane of the rebuild owns kVecPerLane
+// 8-element vectors of it (16 bytes of bf16, 32 bytes of fp32 per vector
+// and array); each lane of the update owns kQuadsPerLane 4-element quads
+// (8 bytes of bf16, 16 bytes of fp32).
 constexpr int kVecPerLane = 2;
 constexpr uint64_t kTileVecs = uint64_t(kBlock) * kVecPerLane;  // vectors per workgroup
 constexpr uint64_t kTileElems = kTileVecs * 8;                  // elements per workgroup
+constexpr int kQuadsPerLane = 4;
+static_assert(uint64_t(kBlock) * kQuadsPerLane * 4 == kTileElems, "the update's quads fill a tile");
 // Shard lookup: one 32-bit word per tile.  Bits 0..30 give the run that
 // holds the tile's first element; bit 31 is set when the tile crosses into
 // another run (lanes then scan forward from that run).

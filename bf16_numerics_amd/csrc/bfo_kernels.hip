@@ -124,17 +124,29 @@ __device__ __forceinline__ uint4 load8Narrow(const uint16_t *p) {
                       uint32_t(p[4]) | (uint32_t(p[5]) << 16), uint32_t(p[6]) | (uint32_t(p[7]) << 16));
 }
 
-// Nontemporal 16-byte loads, for arrays a kernel reads and never writes (the
-// grads in the norm and the update, the master in the rebuild).  Their lines
-// then do not push out the dirty lines of what the previous kernel stored:
-// after an update, the norm's read of the next grads no longer has to drain
-// the update's write-back as it goes (in-step norm on the 1.5B shard 109 ->
-// 66 us), and the whole step ran 2.5% faster although that write-back now
-// lands in the update (3% also when fresh grads are written before every
-// step, as a backward pass would).  Arrays that are read and then written back (m, v,
-// master, the no-master params) keep plain loads: nontemporal ones slowed
-// that mix by 3-8%.
+// Cache policy.  Nontemporal loads and stores (the lines are marked for
+// early eviction from the caches) for data that a kernel touches once:
+//   - the grads, only read, in the norm and in the update: their lines then
+//     do not push out the dirty lines of what the previous kernel stored;
+//     after an update, the norm's read of the next grads no longer has to
+//     drain the update's write-back as it goes (in-step norm on the 1.5B
+//     shard 109 -> 66 us; the whole step 2.5% faster, 3% also when fresh
+//     grads are written before every step, as a backward pass would);
+//   - everything else the update moves, except the params when there is no
+//     master: m, v and the master loaded and stored nontemporally, and the
+//     params (written, never read, when there is a master) stored so.  With
+//     the update's wave-contiguous plan (below) this policy ran 2.1-2.4%
+//     faster than plain m, v and master accesses (1.5B shard, 7B state), and
+//     plan and policy together 1.6-3.3% faster than the plan they replaced
+//     (a lane owning two 8-element vectors, so that each fp32 instruction
+//     covered half of every 32-byte piece), where the same policy had been
+//     3-8% slower than plain accesses.  Without a master the params are read
+//     and written back; nontemporal accesses of them made that update 4%
+//     slower, so they stay plain;
+//   - the rebuild: nontemporal master loads (4-6% faster than plain ones on
+//     its 4 B read + 2 B write pattern) and params stores (a further 4-5%).
 typedef unsigned int U32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int U32x2v __attribute__((ext_vector_type(2)));
 typedef float F32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 loadOnce16(const uint16_t *p, uint64_t vec) {
@@ -142,23 +154,37 @@ __device__ __forceinline__ uint4 loadOnce16(const uint16_t *p, uint64_t vec) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-// The store side of the same rule: with a master, the update writes the bf16
-// params and never reads them, and nontemporal stores made the step 1.1%
-// faster on the 1.5B shard's rank 1 (its params start 32 bytes into a line)
-// and 0.2-0.4% on line-aligned shards.  Without a master the params are read
-// and written back, and nontemporal stores cost 1.1% there; nontemporal
-// stores of m, v and the master gained nothing.  The rebuild, which only
-// writes the params too, gained 4-5% from them.
 __device__ __forceinline__ void storeOnce16(uint16_t *p, uint64_t vec, const uint4 &x) {
     __builtin_nontemporal_store(U32x4v{x.x, x.y, x.z, x.w}, reinterpret_cast<U32x4v *>(p) + vec);
+}
+
+// Loads and stores with the nontemporal hint on or off at compile time.
+template <bool kNt, typename T>
+__device__ __forceinline__ T loadHint(const T *p) {
+    if constexpr (kNt) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool kNt, typename T>
+__device__ __forceinline__ void storeHint(T *p, const T &x) {
+    if constexpr (kNt) __builtin_nontemporal_store(x, p);
+    else *p = x;
+}
+
+// Four consecutive bf16 patterns from a 2-byte-aligned address, packed as in
+// an 8-byte load.
+__device__ __forceinline__ U32x2v load4Narrow(const uint16_t *p) {
+    return U32x2v{uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16)};
 }
 
 // ---------------------------------------------------------------------------
 // Shard plan lookups.
 // ---------------------------------------------------------------------------
+// Where a piece of consecutive shard elements (an 8-element vector of the
+// rebuild and the norm, a 4-element quad of the update) sits.
 struct Place {
-    uint32_t run;   // run holding the vector's first element
-    bool inRun;     // all 8 elements exist and lie in that run
+    uint32_t run;   // run holding the piece's first element
+    bool inRun;     // all its elements exist and lie in that run
     uint64_t addr0; // P/G position of the first element
     uint64_t rng0;  // global index of the first element
 };
@@ -244,15 +270,77 @@ __device__ __forceinline__ float adamwElem(float graw, float &m, float &v, float
 
 enum : int { kNone = 0, kRegular = 1, kSemi = 2, kPerElement = 3 };
 
-// Per-element path of the update: the vector crosses runs or the shard end.
+// ---------------------------------------------------------------------------
+// Fused update.  Workgroup `tile` owns shard-local elements
+// [tile * kTileElems, +kTileElems); wave w of it owns the 1024 elements
+// from 1024 w, and lane t of the wave the kQuadsPerLane quads (4 consecutive
+// elements) at 4 t + 256 k.  Every load and store instruction of a wave so
+// covers one contiguous stretch: 1 KiB of an fp32 array (16 bytes a lane)
+// or 512 bytes of a bf16 one (8 bytes a lane).  A quad is
+//   - regular: in one run, with P and G 16-byte aligned (so the quad's 8
+//     bytes of each are aligned): every array moves as one access;
+//   - semi-regular: in one run, P and G not 16-byte aligned: fp32 state as
+//     16-byte accesses, bf16 P/G per element;
+//   - per element: it crosses runs or the shard end.
+// A quad's four draws are one half of a Philox block when its global index
+// is 0 or 4 mod 8 (the other half belongs to the neighbouring lane, which
+// computes the block again: handing halves between the two lanes measured
+// no faster), and come from one or two blocks otherwise.  All loads are
+// issued before any math.  kScheduled: lr, bias corrections and seed come
+// from steps[*cursor] in device memory instead of the launch arguments, so
+// one recorded launch serves every step; the cursor is read before the data
+// loads are issued and the scalars after, so their round trips overlap.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ Place placeQuad(const ShardView &sv, uint32_t tileWord, uint64_t j0, uint64_t S) {
+    Place pl;
+    if (sv.flatBegin != UINT64_MAX && !(tileWord & kTileMixed)) {
+        pl.run = tileWord;
+        pl.inRun = j0 + 4 <= S;
+        pl.addr0 = j0;
+        pl.rng0 = sv.flatBegin + j0;
+        return pl;
+    }
+    uint32_t k = tileWord & ~kTileMixed;
+    uint64_t runEnd = UINT64_MAX;
+    if (tileWord & kTileMixed) {
+        while (sv.local[k + 1] <= j0) ++k;
+        runEnd = sv.local[k + 1];
+    }
+    pl.run = k;
+    pl.inRun = j0 + 4 <= S && j0 + 4 <= runEnd;
+    const uint64_t off = j0 - sv.local[k];
+    pl.addr0 = sv.addr[k] + off;
+    pl.rng0 = sv.rng[k] + off;
+    return pl;
+}
+
+// Draws of the 4 consecutive global indices rng0 .. rng0+3.
+__device__ __forceinline__ void draws4(uint64_t rng0, uint32_t k0, uint32_t k1, uint32_t d[4]) {
+    const U32x4 a = philox10(rng0 >> 3, k0, k1);
+    const int s = int(rng0 & 7);
+    if ((s & 3) == 0) {
+        const uint32_t lo = s ? a.z : a.x, hi = s ? a.w : a.y;
+        d[0] = lo & 0xFFFFu;
+        d[1] = lo >> 16;
+        d[2] = hi & 0xFFFFu;
+        d[3] = hi >> 16;
+    } else {
+        const U32x4 b = s > 4 ? philox10((rng0 >> 3) + 1, k0, k1) : a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = (s + e) < 8 ? drawOf(a, s + e) : drawOf(b, s + e - 8);
+    }
+}
+
+// Per-element path of the update: elements j0 .. j0+count-1 (stopping at the
+// shard end), which may cross runs.
 template <bool kMaster, int kRound>
 __device__ void adamwElementwise(uint16_t *P, const uint16_t *G, float *M, float *Mom, float *Var, uint64_t j0,
-                                 uint64_t S, const ShardView &sv, uint32_t run, const StepScalars &s,
+                                 int count, uint64_t S, const ShardView &sv, uint32_t run, const StepScalars &s,
                                  float scale, uint32_t key0, uint32_t key1) {
     uint32_t k = run;
     uint64_t cachedGroup = UINT64_MAX;
     U32x4 cached{0u, 0u, 0u, 0u};
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < count; ++e) {
         const uint64_t j = j0 + uint64_t(e);
         if (j >= S) break;
         uint64_t addr, rng;
@@ -276,16 +364,11 @@ __device__ void adamwElementwise(uint16_t *P, const uint16_t *G, float *M, float
     }
 }
 
-// ---------------------------------------------------------------------------
-// Fused update.  Workgroup `tile` owns shard-local vectors
-// [tile * kTileVecs, +kTileVecs); lane t takes vectors t and t + 256 of it,
-// so each load instruction of a wave covers 1 KiB (bf16) or 2 KiB (fp32) of
-// contiguous memory.  All loads of the run-aligned vectors are issued before
-// any math.  kScheduled: lr, bias corrections and seed come from
-// steps[*cursor] in device memory instead of the launch arguments, so one
-// recorded launch serves every step; the cursor is read before the data
-// loads are issued and the scalars after, so their round trips overlap.
-// ---------------------------------------------------------------------------
+// Shard-local element of lane threadIdx.x's first quad in workgroup `tile`.
+__device__ __forceinline__ uint64_t quadBase(uint64_t tile) {
+    return tile * kTileElems + uint64_t(threadIdx.x >> 6) * 1024 + uint64_t(threadIdx.x & 63) * 4;
+}
+
 // The update of one tile by one workgroup (the body of adamwTileKernel and
 // of the one-launch small step).  cur: the schedule cursor, read by the
 // caller (kScheduled only).
@@ -297,38 +380,33 @@ __device__ __forceinline__ void adamwTile(uint16_t *__restrict__ P, const uint16
                                           const bfo_step_scalars *__restrict__ steps, uint64_t nsteps,
                                           uint64_t cur) {
     const uint32_t tileWord = sv.tile[tile];
+    const uint64_t base = quadBase(tile);
 
-    uint4 gv[kVecPerLane], pv[kVecPerLane];
-    float4 ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
-    float4 wa[kVecPerLane], wb[kVecPerLane];
-    Place pl[kVecPerLane];
-    int mode[kVecPerLane];
+    U32x2v gq[kQuadsPerLane], pq[kQuadsPerLane];
+    F32x4 mq[kQuadsPerLane], vq[kQuadsPerLane], wq[kQuadsPerLane];
+    Place pl[kQuadsPerLane];
+    int mode[kQuadsPerLane];
 
 #pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+    for (int k = 0; k < kQuadsPerLane; ++k) {
+        const uint64_t j0 = base + uint64_t(k) * 256;
         mode[k] = kNone;
-        if (q * 8 >= S) continue;
-        pl[k] = placeVector(sv, tileWord, q * 8, S);
+        if (j0 >= S) continue;
+        pl[k] = placeQuad(sv, tileWord, j0, S);
         if (!pl[k].inRun) {
             mode[k] = kPerElement;
             continue;
         }
-        mode[k] = (pgVec && (pl[k].addr0 & 7) == 0) ? kRegular : kSemi;
-        ma[k] = reinterpret_cast<const float4 *>(Mom)[2 * q];
-        mb[k] = reinterpret_cast<const float4 *>(Mom)[2 * q + 1];
-        va[k] = reinterpret_cast<const float4 *>(Var)[2 * q];
-        vb[k] = reinterpret_cast<const float4 *>(Var)[2 * q + 1];
-        if constexpr (kMaster) {
-            wa[k] = reinterpret_cast<const float4 *>(M)[2 * q];
-            wb[k] = reinterpret_cast<const float4 *>(M)[2 * q + 1];
-        }
+        mode[k] = (pgVec && (pl[k].addr0 & 3) == 0) ? kRegular : kSemi;
+        mq[k] = loadHint<true>(reinterpret_cast<const F32x4 *>(Mom + j0));
+        vq[k] = loadHint<true>(reinterpret_cast<const F32x4 *>(Var + j0));
+        if constexpr (kMaster) wq[k] = loadHint<true>(reinterpret_cast<const F32x4 *>(M + j0));
         if (mode[k] == kRegular) {
-            gv[k] = loadOnce16(G, pl[k].addr0 >> 3);
-            if constexpr (!kMaster) pv[k] = reinterpret_cast<const uint4 *>(P)[pl[k].addr0 >> 3];
+            gq[k] = loadHint<true>(reinterpret_cast<const U32x2v *>(G + pl[k].addr0));
+            if constexpr (!kMaster) pq[k] = loadHint<false>(reinterpret_cast<const U32x2v *>(P + pl[k].addr0));
         } else {
-            gv[k] = load8Narrow(G + pl[k].addr0);
-            if constexpr (!kMaster) pv[k] = load8Narrow(P + pl[k].addr0);
+            gq[k] = load4Narrow(G + pl[k].addr0);
+            if constexpr (!kMaster) pq[k] = load4Narrow(P + pl[k].addr0);
         }
     }
     if constexpr (kScheduled) {
@@ -342,60 +420,43 @@ __device__ __forceinline__ void adamwTile(uint16_t *__restrict__ P, const uint16
     }
 
 #pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
+    for (int k = 0; k < kQuadsPerLane; ++k) {
         if (mode[k] == kNone) continue;
-        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+        const uint64_t j0 = base + uint64_t(k) * 256;
         if (mode[k] == kPerElement) {
-            adamwElementwise<kMaster, kRound>(P, G, M, Mom, Var, q * 8, S, sv, pl[k].run, s, scale, key0, key1);
+            adamwElementwise<kMaster, kRound>(P, G, M, Mom, Var, j0, 4, S, sv, pl[k].run, s, scale, key0, key1);
             continue;
         }
-        uint32_t draws[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        if constexpr (kRound == BFO_ROUND_SR) draws8(pl[k].rng0, key0, key1, draws);
+        uint32_t draws[4] = {0u, 0u, 0u, 0u};
+        if constexpr (kRound == BFO_ROUND_SR) draws4(pl[k].rng0, key0, key1, draws);
         const float w = sv.flag[pl[k].run] ? s.wd : 0.0f;
 
-        float gr[8] = {bf16Lo(gv[k].x), bf16Hi(gv[k].x), bf16Lo(gv[k].y), bf16Hi(gv[k].y),
-                       bf16Lo(gv[k].z), bf16Hi(gv[k].z), bf16Lo(gv[k].w), bf16Hi(gv[k].w)};
-        float mm[8] = {ma[k].x, ma[k].y, ma[k].z, ma[k].w, mb[k].x, mb[k].y, mb[k].z, mb[k].w};
-        float vv[8] = {va[k].x, va[k].y, va[k].z, va[k].w, vb[k].x, vb[k].y, vb[k].z, vb[k].w};
-        float old[8];
+        const float gr[4] = {bf16Lo(gq[k].x), bf16Hi(gq[k].x), bf16Lo(gq[k].y), bf16Hi(gq[k].y)};
+        float mm[4] = {mq[k].x, mq[k].y, mq[k].z, mq[k].w};
+        float vv[4] = {vq[k].x, vq[k].y, vq[k].z, vq[k].w};
+        float old[4];
         if constexpr (kMaster) {
-            old[0] = wa[k].x; old[1] = wa[k].y; old[2] = wa[k].z; old[3] = wa[k].w;
-            old[4] = wb[k].x; old[5] = wb[k].y; old[6] = wb[k].z; old[7] = wb[k].w;
+            old[0] = wq[k].x; old[1] = wq[k].y; old[2] = wq[k].z; old[3] = wq[k].w;
         } else {
-            old[0] = bf16Lo(pv[k].x); old[1] = bf16Hi(pv[k].x);
-            old[2] = bf16Lo(pv[k].y); old[3] = bf16Hi(pv[k].y);
-            old[4] = bf16Lo(pv[k].z); old[5] = bf16Hi(pv[k].z);
-            old[6] = bf16Lo(pv[k].w); old[7] = bf16Hi(pv[k].w);
+            old[0] = bf16Lo(pq[k].x); old[1] = bf16Hi(pq[k].x); old[2] = bf16Lo(pq[k].y); old[3] = bf16Hi(pq[k].y);
         }
-        float pn[8];
-        uint32_t hb[8];
+        float pn[4];
+        uint32_t hb[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             pn[e] = adamwElem(gr[e], mm[e], vv[e], old[e], w, s, scale);
             hb[e] = writeBack<kRound>(pn[e], draws[e]);
         }
-        reinterpret_cast<float4 *>(Mom)[2 * q] = make_float4(mm[0], mm[1], mm[2], mm[3]);
-        reinterpret_cast<float4 *>(Mom)[2 * q + 1] = make_float4(mm[4], mm[5], mm[6], mm[7]);
-        reinterpret_cast<float4 *>(Var)[2 * q] = make_float4(vv[0], vv[1], vv[2], vv[3]);
-        reinterpret_cast<float4 *>(Var)[2 * q + 1] = make_float4(vv[4], vv[5], vv[6], vv[7]);
-        if constexpr (kMaster) {
-            reinterpret_cast<float4 *>(M)[2 * q] = make_float4(pn[0], pn[1], pn[2], pn[3]);
-            reinterpret_cast<float4 *>(M)[2 * q + 1] = make_float4(pn[4], pn[5], pn[6], pn[7]);
-        }
+        storeHint<true>(reinterpret_cast<F32x4 *>(Mom + j0), F32x4{mm[0], mm[1], mm[2], mm[3]});
+        storeHint<true>(reinterpret_cast<F32x4 *>(Var + j0), F32x4{vv[0], vv[1], vv[2], vv[3]});
+        if constexpr (kMaster) storeHint<true>(reinterpret_cast<F32x4 *>(M + j0), F32x4{pn[0], pn[1], pn[2], pn[3]});
         if (mode[k] == kRegular) {
-            uint4 out;
-            out.x = hb[0] | (hb[1] << 16);
-            out.y = hb[2] | (hb[3] << 16);
-            out.z = hb[4] | (hb[5] << 16);
-            out.w = hb[6] | (hb[7] << 16);
-            if constexpr (kMaster)
-                storeOnce16(P, pl[k].addr0 >> 3, out);
-            else
-                reinterpret_cast<uint4 *>(P)[pl[k].addr0 >> 3] = out;
+            storeHint<kMaster>(reinterpret_cast<U32x2v *>(P + pl[k].addr0),
+                               U32x2v{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)});
         } else {
             uint16_t *p = P + pl[k].addr0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = uint16_t(hb[e]);
+            for (int e = 0; e < 4; ++e) p[e] = uint16_t(hb[e]);
         }
     }
 }
@@ -417,16 +478,16 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
 
 // ---------------------------------------------------------------------------
 // Measurement kernel: the update's memory traffic without its arithmetic.
-// Same tile, lane and vector plan as the 16-byte path of adamwTileKernel
-// and the same cache policies (nontemporal grads loads and, with a master,
-// nontemporal params stores).  kMode:
+// Same tile, lane and quad plan as the regular path of adamwTileKernel and
+// the same cache policies (everything nontemporal except, without a master,
+// the params).  kMode:
 //   BFO_MIX_BOTH: the update's reads and writes (with a master: reads G, m,
 //     v, M and writes m, v, M, P; without: reads G, P, m, v and writes P, m,
 //     v), each output a bit-XOR of its inputs and the key, so nothing can be
 //     elided; key 0 leaves m, v and M bitwise as they were;
 //   BFO_MIX_READS: the update's reads alone; the loaded words are folded
 //     into one 64-bit value per lane, which is compared with a constant: on
-//     a match (odds 2^-64 per lane) the lane stores the m vector it loaded
+//     a match (odds 2^-64 per lane) the lane stores the m quad it loaded
 //     back unchanged, so the loads stay and no state changes;
 //   BFO_MIX_WRITES: the update's writes alone, of words made from the key
 //     and the element index (m, v, M and P are overwritten).
@@ -440,46 +501,40 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
                                                           float *__restrict__ Var, uint64_t count, uint32_t key,
                                                           uint64_t tileBase) {
     constexpr bool kRead = kMode != BFO_MIX_WRITES;
-    const uint64_t tile = tileBase + blockIdx.x;
-    uint4 gv[kVecPerLane], pv[kVecPerLane], ma[kVecPerLane], mb[kVecPerLane], va[kVecPerLane], vb[kVecPerLane];
-    uint4 wa[kVecPerLane], wb[kVecPerLane];
-    int mode[kVecPerLane];
+    const uint64_t base = quadBase(tileBase + blockIdx.x);
+    U32x2v gq[kQuadsPerLane], pq[kQuadsPerLane];
+    U32x4v mq[kQuadsPerLane], vq[kQuadsPerLane], wq[kQuadsPerLane];
+    int mode[kQuadsPerLane];
 #pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-        mode[k] = q * 8 + 8 <= count ? kRegular : (q * 8 < count ? kPerElement : kNone);
+    for (int k = 0; k < kQuadsPerLane; ++k) {
+        const uint64_t j0 = base + uint64_t(k) * 256;
+        mode[k] = j0 + 4 <= count ? kRegular : (j0 < count ? kPerElement : kNone);
         if (mode[k] != kRegular || !kRead) continue;
-        gv[k] = loadOnce16(G, q);
-        ma[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q];
-        mb[k] = reinterpret_cast<const uint4 *>(Mom)[2 * q + 1];
-        va[k] = reinterpret_cast<const uint4 *>(Var)[2 * q];
-        vb[k] = reinterpret_cast<const uint4 *>(Var)[2 * q + 1];
-        if constexpr (kMaster) {
-            wa[k] = reinterpret_cast<const uint4 *>(M)[2 * q];
-            wb[k] = reinterpret_cast<const uint4 *>(M)[2 * q + 1];
-        } else {
-            pv[k] = reinterpret_cast<const uint4 *>(P)[q];
-        }
+        gq[k] = loadHint<true>(reinterpret_cast<const U32x2v *>(G + j0));
+        mq[k] = loadHint<true>(reinterpret_cast<const U32x4v *>(Mom + j0));
+        vq[k] = loadHint<true>(reinterpret_cast<const U32x4v *>(Var + j0));
+        if constexpr (kMaster) wq[k] = loadHint<true>(reinterpret_cast<const U32x4v *>(M + j0));
+        else pq[k] = loadHint<false>(reinterpret_cast<const U32x2v *>(P + j0));
     }
     if constexpr (kMode == BFO_MIX_READS) {
 #pragma unroll
-        for (int k = 0; k < kVecPerLane; ++k) {
+        for (int k = 0; k < kQuadsPerLane; ++k) {
             if (mode[k] != kRegular) continue;
-            uint4 x = gv[k] ^ ma[k] ^ mb[k] ^ va[k] ^ vb[k];
-            if constexpr (kMaster) x = x ^ wa[k] ^ wb[k];
-            else x = x ^ pv[k];
-            const uint64_t folded = (uint64_t(x.x ^ x.z) << 32) | uint64_t(x.y ^ x.w);
-            const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
-            if (folded == (0x9E3779B97F4A7C15ull ^ key)) reinterpret_cast<uint4 *>(Mom)[2 * q] = ma[k];
+            U32x4v x = mq[k] ^ vq[k];
+            if constexpr (kMaster) x = x ^ wq[k];
+            else x = x ^ U32x4v{pq[k].x, pq[k].y, 0u, 0u};
+            const uint64_t folded = (uint64_t(x.x ^ x.z ^ gq[k].x) << 32) | uint64_t(x.y ^ x.w ^ gq[k].y);
+            const uint64_t j0 = base + uint64_t(k) * 256;
+            if (folded == (0x9E3779B97F4A7C15ull ^ key)) *reinterpret_cast<U32x4v *>(Mom + j0) = mq[k];
         }
         return;
     }
     const uint32_t key2 = (key & 0xFFFFu) | (key << 16);
 #pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-        const uint64_t q = tile * kTileVecs + uint64_t(k) * kBlock + threadIdx.x;
+    for (int k = 0; k < kQuadsPerLane; ++k) {
+        const uint64_t j0 = base + uint64_t(k) * 256;
         if (mode[k] == kPerElement && kMode == BFO_MIX_BOTH) {
-            for (uint64_t j = q * 8; j < count; ++j) {
+            for (uint64_t j = j0; j < count; ++j) {
                 Mom[j] = __uint_as_float(__float_as_uint(Mom[j]) ^ key);
                 Var[j] = __uint_as_float(__float_as_uint(Var[j]) ^ key);
                 if constexpr (kMaster) {
@@ -492,7 +547,7 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
             continue;
         }
         if (mode[k] == kPerElement) {
-            for (uint64_t j = q * 8; j < count; ++j) {
+            for (uint64_t j = j0; j < count; ++j) {
                 const uint32_t x = key ^ uint32_t(j);
                 Mom[j] = __uint_as_float(x);
                 Var[j] = __uint_as_float(x ^ 1u);
@@ -503,28 +558,20 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
         }
         if (mode[k] != kRegular) continue;
         if constexpr (kMode == BFO_MIX_WRITES) {
-            const uint32_t x = key ^ uint32_t(q * 8);
-            ma[k] = make_uint4(x, x + 1, x + 2, x + 3);
-            mb[k] = make_uint4(x + 4, x + 5, x + 6, x + 7);
-            va[k] = ma[k] ^ make_uint4(1u, 1u, 1u, 1u);
-            vb[k] = mb[k] ^ make_uint4(1u, 1u, 1u, 1u);
-            wa[k] = ma[k] ^ make_uint4(2u, 2u, 2u, 2u);
-            wb[k] = mb[k] ^ make_uint4(2u, 2u, 2u, 2u);
-            gv[k] = make_uint4(x, x ^ 3u, x ^ 5u, x ^ 7u);
-            pv[k] = make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t x = key ^ uint32_t(j0);
+            mq[k] = U32x4v{x, x + 1, x + 2, x + 3};
+            vq[k] = mq[k] ^ 1u;
+            wq[k] = mq[k] ^ 2u;
+            gq[k] = U32x2v{x, x ^ 5u};
+            pq[k] = U32x2v{0u, 0u};
         }
-        const uint4 kk = make_uint4(key, key, key, key);
-        const uint4 k2 = make_uint4(key2, key2, key2, key2);
-        reinterpret_cast<uint4 *>(Mom)[2 * q] = ma[k] ^ kk;
-        reinterpret_cast<uint4 *>(Mom)[2 * q + 1] = mb[k] ^ kk;
-        reinterpret_cast<uint4 *>(Var)[2 * q] = va[k] ^ kk;
-        reinterpret_cast<uint4 *>(Var)[2 * q + 1] = vb[k] ^ kk;
+        storeHint<true>(reinterpret_cast<U32x4v *>(Mom + j0), mq[k] ^ key);
+        storeHint<true>(reinterpret_cast<U32x4v *>(Var + j0), vq[k] ^ key);
         if constexpr (kMaster) {
-            reinterpret_cast<uint4 *>(M)[2 * q] = wa[k] ^ kk;
-            reinterpret_cast<uint4 *>(M)[2 * q + 1] = wb[k] ^ kk;
-            storeOnce16(P, q, gv[k] ^ k2);
+            storeHint<true>(reinterpret_cast<U32x4v *>(M + j0), wq[k] ^ key);
+            storeHint<true>(reinterpret_cast<U32x2v *>(P + j0), gq[k] ^ key2);
         } else {
-            reinterpret_cast<uint4 *>(P)[q] = pv[k] ^ gv[k] ^ k2;
+            storeHint<false>(reinterpret_cast<U32x2v *>(P + j0), pq[k] ^ gq[k] ^ key2);
         }
     }
 }
