@@ -338,8 +338,9 @@ int bfo_decay_mask_dump(bfo_table table, uint8_t *out, void *stream);
 
 /* Measurement export: the update's memory traffic with none of its
  * arithmetic, for an achievable-bandwidth ceiling measured the same way as
- * the update, in the update's 16-byte vector and workgroup plan and with its
- * cache policies.  For j < count (device arrays of count elements):
+ * the update, in the update's workgroup and lane plan (4-element quads:
+ * 16-byte fp32 and 8-byte bf16 accesses) and with its cache policies.  For
+ * j < count (device arrays of count elements):
  *   BFO_MIX_BOTH -- with a master: m[j], v[j], master[j] ^= key (as 32-bit
  *     patterns) and params[j] = grads[j] ^ (key & 0xFFFF): 14 bytes read and
  *     14 written per element, as the master update; master == NULL: m[j],
