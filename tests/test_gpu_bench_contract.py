@@ -41,6 +41,8 @@ def test_bench_line_follows_the_contract():
     assert cb["kind"] == "oracle" and cb["unit"] == "Gparams/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["sample"], str) and cb["sample"]
     assert d["ceiling"]["achieved"] > 0 and d["rebuild"]["achieved"] > 0
+    # the read-only settle passes ran before the warm-up steps, for about the default two seconds
+    assert d["settle"]["passes"] > 0 and 1.9 <= d["settle"]["seconds"] <= 10.0
 
 
 def test_bench_graph_mode_line():
