@@ -842,6 +842,16 @@ def test_full_size_llama7b(bfo):
     assert got[2] < 1.0
 
 
+@pytest.mark.timeout(600)
+def test_full_size_llama7b_no_master(bfo):
+    # The no-master update (old weights read from the bf16 params; lanes pair
+    # up to share Philox blocks) over the whole 6.74e9-element state, global
+    # indices past 2^32: steps 1 and 2 against the oracle on every element.
+    w = W.llama7b()
+    got = full_size_step(bfo, w, 0, steps=2, master=False)
+    print(f"llama7b no master: norm {got[1]:.6f} scale {got[2]:.6f}", flush=True)
+
+
 def test_full_size_gpt2_1p5b_eight_shards_equal_the_unsharded_step(bfo):
     # The ZeRO-1 invariant at full size: the 8 ranks' flat shards, stepped
     # with the global clip scale into one shared param buffer, reproduce the
