@@ -411,6 +411,36 @@ __device__ __forceinline__ uint64_t quadBase(uint64_t tile) {
     return tile * kTileElems + uint64_t(threadIdx.x >> 6) * 1024 + uint64_t(threadIdx.x & 63) * 4;
 }
 
+// Draws of quad k: the lane pair's shared blocks when the wave paired, else
+// the quad's own block(s).
+template <int kRound>
+__device__ __forceinline__ void quadDraws(bool paired, uint32_t lo, uint32_t hi, uint64_t rng0, uint32_t key0,
+                                          uint32_t key1, uint32_t d[4]) {
+    if (paired) {
+        d[0] = lo & 0xFFFFu;
+        d[1] = lo >> 16;
+        d[2] = hi & 0xFFFFu;
+        d[3] = hi >> 16;
+    } else if constexpr (kRound == BFO_ROUND_SR) {
+        draws4(rng0, key0, key1, d);
+    } else {
+        d[0] = d[1] = d[2] = d[3] = 0u;
+    }
+}
+
+// The four elements of a quad: m and v updated in place, the new fp32
+// weights in pn and their bf16 patterns in hb.
+template <int kRound>
+__device__ __forceinline__ void stepQuad(const float gr[4], float mm[4], float vv[4], const float old[4], float w,
+                                         const StepScalars &s, float scale, const uint32_t d[4], float pn[4],
+                                         uint32_t hb[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pn[e] = adamwElem(gr[e], mm[e], vv[e], old[e], w, s, scale);
+        hb[e] = writeBack<kRound>(pn[e], d[e]);
+    }
+}
+
 // The update of one tile by one workgroup (the body of adamwTileKernel and
 // of the one-launch small step).  cur: the schedule cursor, read by the
 // caller (kScheduled only).
@@ -475,15 +505,8 @@ __device__ __forceinline__ void adamwTile(uint16_t *__restrict__ P, const uint16
             adamwElementwise<kMaster, kRound>(P, G, M, Mom, Var, j0, 4, S, sv, pl[k].run, s, scale, key0, key1);
             continue;
         }
-        uint32_t draws[4] = {0u, 0u, 0u, 0u};
-        if (kPairDraws && paired) {
-            draws[0] = pairLo[k] & 0xFFFFu;
-            draws[1] = pairLo[k] >> 16;
-            draws[2] = pairHi[k] & 0xFFFFu;
-            draws[3] = pairHi[k] >> 16;
-        } else if constexpr (kRound == BFO_ROUND_SR) {
-            draws4(pl[k].rng0, key0, key1, draws);
-        }
+        uint32_t draws[4];
+        quadDraws<kRound>(kPairDraws && paired, pairLo[k], pairHi[k], pl[k].rng0, key0, key1, draws);
         const float w = sv.flag[pl[k].run] ? s.wd : 0.0f;
 
         const float gr[4] = {bf16Lo(gq[k].x), bf16Hi(gq[k].x), bf16Lo(gq[k].y), bf16Hi(gq[k].y)};
@@ -497,11 +520,7 @@ __device__ __forceinline__ void adamwTile(uint16_t *__restrict__ P, const uint16
         }
         float pn[4];
         uint32_t hb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            pn[e] = adamwElem(gr[e], mm[e], vv[e], old[e], w, s, scale);
-            hb[e] = writeBack<kRound>(pn[e], draws[e]);
-        }
+        stepQuad<kRound>(gr, mm, vv, old, w, s, scale, draws, pn, hb);
         storeHint<true>(reinterpret_cast<F32x4 *>(Mom + j0), F32x4{mm[0], mm[1], mm[2], mm[3]});
         storeHint<true>(reinterpret_cast<F32x4 *>(Var + j0), F32x4{vv[0], vv[1], vv[2], vv[3]});
         if constexpr (kMaster) storeHint<true>(reinterpret_cast<F32x4 *>(M + j0), F32x4{pn[0], pn[1], pn[2], pn[3]});
@@ -516,6 +535,117 @@ __device__ __forceinline__ void adamwTile(uint16_t *__restrict__ P, const uint16
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same update for a tile of a flat shard that lies in one run, with P and
+// G 16-byte aligned (almost every tile of a flat shard): the five arrays are
+// addressed through buffer resources based at the tile's first element, so a
+// lane's addresses are 32-bit offsets from workgroup-uniform bases instead
+// of 64-bit pointer arithmetic per access, and the cache policy (the
+// nontemporal bit) rides on each buffer instruction.  Same quads, same
+// order of operations and same draws as adamwTile, so the same bits.
+// Measured against adamwTile on these tiles: 0.3-0.6% faster with a master
+// (7B state, 1.5B shards at both params alignments), equal without one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tileResource(const void *base, uint32_t bytes) {
+    // raw buffer: no stride, `bytes` records, the gfx9 default format word
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+constexpr int kPolicyNt = 2;     // cache-policy operand of the buffer builtins: the nontemporal bit
+constexpr int kPolicyPlain = 0;
+
+template <bool kMaster, int kRound, bool kScheduled>
+__device__ __forceinline__ void adamwTileFlat(uint16_t *__restrict__ P, const uint16_t *__restrict__ G,
+                                              float *__restrict__ M, float *__restrict__ Mom,
+                                              float *__restrict__ Var, uint64_t S, const ShardView &sv,
+                                              StepScalars s, float scale, uint32_t key0, uint32_t key1,
+                                              uint64_t tile, const bfo_step_scalars *__restrict__ steps,
+                                              uint64_t nsteps, uint64_t cur) {
+    constexpr bool kPairDraws = kRound == BFO_ROUND_SR && !kMaster;
+    constexpr int kParamsPolicy = kMaster ? kPolicyNt : kPolicyPlain;
+    const uint32_t run = sv.tile[tile];
+    const uint64_t e0 = tile * kTileElems;
+    const uint32_t n = uint32_t(S - e0 < kTileElems ? S - e0 : kTileElems);   // the tile's elements in the shard
+    const __amdgpu_buffer_rsrc_t rm = tileResource(Mom + e0, n * 4), rv = tileResource(Var + e0, n * 4);
+    const __amdgpu_buffer_rsrc_t rM = tileResource(kMaster ? M + e0 : Mom + e0, n * 4);
+    const __amdgpu_buffer_rsrc_t rG = tileResource(G + e0, n * 2), rP = tileResource(P + e0, n * 2);
+    const uint32_t lane = (threadIdx.x >> 6) * 1024 + (threadIdx.x & 63) * 4;   // quadBase within the tile
+
+    U32x2v gq[kQuadsPerLane], pq[kQuadsPerLane];
+    U32x4v mq[kQuadsPerLane], vq[kQuadsPerLane], wq[kQuadsPerLane];
+    Place pl[kQuadsPerLane];
+    int mode[kQuadsPerLane];
+
+#pragma unroll
+    for (int k = 0; k < kQuadsPerLane; ++k) {
+        const uint32_t off = lane + 256u * k;
+        mode[k] = off + 4 <= n ? kRegular : (off < n ? kPerElement : kNone);
+        pl[k].run = run;
+        pl[k].inRun = mode[k] == kRegular;
+        pl[k].addr0 = e0 + off;
+        pl[k].rng0 = sv.flatBegin + e0 + off;
+        if (mode[k] != kRegular) continue;
+        mq[k] = __builtin_amdgcn_raw_buffer_load_b128(rm, off * 4, 0, kPolicyNt);
+        vq[k] = __builtin_amdgcn_raw_buffer_load_b128(rv, off * 4, 0, kPolicyNt);
+        if constexpr (kMaster) wq[k] = __builtin_amdgcn_raw_buffer_load_b128(rM, off * 4, 0, kPolicyNt);
+        gq[k] = __builtin_amdgcn_raw_buffer_load_b64(rG, off * 2, 0, kPolicyNt);
+        if constexpr (!kMaster) pq[k] = __builtin_amdgcn_raw_buffer_load_b64(rP, off * 2, 0, kParamsPolicy);
+    }
+    if constexpr (kScheduled) {
+        if (cur >= nsteps) return;    // past the scheduled steps: no update (nothing stored yet)
+        const bfo_step_scalars st = steps[cur];
+        s.lr = st.lr;
+        s.bc1 = st.bc1;
+        s.bc2 = st.bc2;
+        key0 = uint32_t(st.seed);
+        key1 = uint32_t(st.seed >> 32);
+    }
+
+    uint32_t pairLo[kQuadsPerLane], pairHi[kQuadsPerLane];
+    bool paired = false;
+    if constexpr (kPairDraws) paired = pairDraws(pl, mode, key0, key1, pairLo, pairHi);
+    const float w = sv.flag[run] ? s.wd : 0.0f;
+
+#pragma unroll
+    for (int k = 0; k < kQuadsPerLane; ++k) {
+        if (mode[k] == kNone) continue;
+        const uint32_t off = lane + 256u * k;
+        if (mode[k] == kPerElement) {
+            adamwElementwise<kMaster, kRound>(P, G, M, Mom, Var, e0 + off, 4, S, sv, run, s, scale, key0, key1);
+            continue;
+        }
+        uint32_t draws[4];
+        quadDraws<kRound>(kPairDraws && paired, pairLo[k], pairHi[k], pl[k].rng0, key0, key1, draws);
+        const float gr[4] = {bf16Lo(gq[k].x), bf16Hi(gq[k].x), bf16Lo(gq[k].y), bf16Hi(gq[k].y)};
+        float mm[4] = {__uint_as_float(mq[k].x), __uint_as_float(mq[k].y), __uint_as_float(mq[k].z),
+                       __uint_as_float(mq[k].w)};
+        float vv[4] = {__uint_as_float(vq[k].x), __uint_as_float(vq[k].y), __uint_as_float(vq[k].z),
+                       __uint_as_float(vq[k].w)};
+        float old[4];
+        if constexpr (kMaster) {
+            old[0] = __uint_as_float(wq[k].x); old[1] = __uint_as_float(wq[k].y);
+            old[2] = __uint_as_float(wq[k].z); old[3] = __uint_as_float(wq[k].w);
+        } else {
+            old[0] = bf16Lo(pq[k].x); old[1] = bf16Hi(pq[k].x); old[2] = bf16Lo(pq[k].y); old[3] = bf16Hi(pq[k].y);
+        }
+        float pn[4];
+        uint32_t hb[4];
+        stepQuad<kRound>(gr, mm, vv, old, w, s, scale, draws, pn, hb);
+        __builtin_amdgcn_raw_buffer_store_b128(U32x4v{__float_as_uint(mm[0]), __float_as_uint(mm[1]),
+                                                      __float_as_uint(mm[2]), __float_as_uint(mm[3])},
+                                               rm, off * 4, 0, kPolicyNt);
+        __builtin_amdgcn_raw_buffer_store_b128(U32x4v{__float_as_uint(vv[0]), __float_as_uint(vv[1]),
+                                                      __float_as_uint(vv[2]), __float_as_uint(vv[3])},
+                                               rv, off * 4, 0, kPolicyNt);
+        if constexpr (kMaster)
+            __builtin_amdgcn_raw_buffer_store_b128(U32x4v{__float_as_uint(pn[0]), __float_as_uint(pn[1]),
+                                                          __float_as_uint(pn[2]), __float_as_uint(pn[3])},
+                                                   rM, off * 4, 0, kPolicyNt);
+        __builtin_amdgcn_raw_buffer_store_b64(U32x2v{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)}, rP, off * 2, 0,
+                                              kParamsPolicy);
+    }
+}
+
 template <bool kMaster, int kRound, bool kScheduled>
 __global__ __launch_bounds__(kBlock) void adamwTileKernel(
     uint16_t *__restrict__ P, const uint16_t *__restrict__ G, float *__restrict__ M,
@@ -527,8 +657,13 @@ __global__ __launch_bounds__(kBlock) void adamwTileKernel(
     uint64_t cur = 0;
     if constexpr (kScheduled) cur = *cursor;
     const float scale = scalePtr ? *scalePtr : 1.0f;
-    adamwTile<kMaster, kRound, kScheduled>(P, G, M, Mom, Var, S, sv, pgVec, s, scale, key0, key1,
-                                           tileBase + blockIdx.x, steps, nsteps, cur);
+    const uint64_t tile = tileBase + blockIdx.x;
+    if (sv.flatBegin != UINT64_MAX && pgVec && !(sv.tile[tile] & kTileMixed))
+        adamwTileFlat<kMaster, kRound, kScheduled>(P, G, M, Mom, Var, S, sv, s, scale, key0, key1, tile, steps,
+                                                   nsteps, cur);
+    else
+        adamwTile<kMaster, kRound, kScheduled>(P, G, M, Mom, Var, S, sv, pgVec, s, scale, key0, key1, tile, steps,
+                                               nsteps, cur);
 }
 
 // ---------------------------------------------------------------------------
