@@ -1,21 +1,23 @@
 // bfo_kernels.hip -- gfx950 kernels of the mixed-precision AdamW step.
 //
 // Every kernel here is bound by HBM bandwidth: each element is touched once
-// per launch, so the design goal is full-width (16-byte) coalesced loads and
-// stores, several in flight per lane, and enough workgroups (>> 256 CUs) to
-// keep every channel busy.  Nothing is a contraction, so there is no MFMA.
+// per launch, so the design goal is full-width coalesced loads and stores
+// (every wave instruction over one contiguous stretch where the plan allows),
+// several in flight per lane, and enough workgroups (>> 256 CUs) to keep
+// every channel busy.  Nothing is a contraction, so there is no MFMA.
 //
 // Shard plan.  The shard's S elements are shard-local positions j; runs map
 // them to positions in the caller's params/grads arrays (addr) and to global
 // indices of the flat buffer (rng, which keys the rounding draws).  Work is
-// cut into 8-element vectors at shard-local positions 8q:
-//   - regular: the vector lies in one run and P/G are 16-byte aligned at its
-//     address: every array moves as 16-byte accesses (the common case);
-//   - semi-regular: one run, but P/G not 16-byte aligned there (misaligned
-//     flat shards): fp32 state as 16-byte accesses, bf16 P/G per element;
-//   - per element: the vector crosses runs or the shard end.
-// A vector's draws come from one Philox block when its global index is
-// 8-aligned and from two otherwise.
+// cut into pieces of consecutive elements -- 4-element quads in the update,
+// 8-element vectors in the rebuild and the norm -- and each piece is
+//   - regular: it lies in one run and P/G are 16-byte aligned: every array
+//     moves as one full-width access per piece (the common case);
+//   - semi-regular: one run, but P/G not 16-byte aligned (misaligned flat
+//     shards): fp32 state as full-width accesses, bf16 P/G per element;
+//   - per element: the piece crosses runs or the shard end.
+// A piece's draws come from one Philox block (eight consecutive global
+// indices) when it sits inside one and from two otherwise.
 //
 // Floating point.  The update is a fixed sequence of binary32 operations
 // (one IEEE operation per line of the per-element function), built with
@@ -767,10 +769,13 @@ __global__ __launch_bounds__(kBlock) void streamMixKernel(uint16_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Rebuild bf16 weights from the master: P = SR(M, draw) (or RNE(M)), same
-// vector plan.  The master is only read and the params only written here:
-// nontemporal loads (4-6% faster than plain ones on this 4 B read + 2 B
-// write pattern) and nontemporal stores (a further 4-5%).
+// Rebuild bf16 weights from the master: P = SR(M, draw) (or RNE(M)).  One
+// workgroup per 4,096-element tile; lane t takes 8-element vectors t and
+// t + 256 of it (16-byte params stores, 32 bytes of master per vector: one
+// Philox block per vector; the update's quad plan, which needs a block per
+// quad, measured slower here).  The master is only read and the params only
+// written here: nontemporal loads (4-6% faster than plain ones on this
+// 4 B read + 2 B write pattern) and nontemporal stores (a further 4-5%).
 // ---------------------------------------------------------------------------
 template <int kRound>
 __global__ __launch_bounds__(kBlock) void masterToBf16Kernel(const float *__restrict__ M,
